@@ -1,0 +1,404 @@
+"""Plain, slow CPU oracle of the ConvRot W4A8 codebook linear layer (NumPy).
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring.  Only ``tests/``,
+``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline`` leg may use it.
+
+Sources.  Each function cites the page and the function or section it follows:
+
+  [AT]  ai-toolkit, ``toolkit/util/convrot_w4a8_quant.py`` (the ConvRot W4A8
+        codebook backend, qtype ``convrotw4a8``): storage contract in the module
+        docstring, ``FIXED_CODEBOOK``, ``W4A8_SAT``, ``_pack_codes``,
+        ``_unpack_codes``, ``unpack_w4a8_eager``, ``_assign_grid``,
+        ``_assign_codes``, ``grid_levels``, ``_quantize_rotated_rows``,
+        ``quantize_w4a8_rotated``, the activation-quant and GEMV Triton kernels
+        (their arithmetic, not their tiling) and ``dequantize_w4a8``.
+  [H3]  h3-rs 0.2.0, ``src/weights.rs``: ``fn hadamard`` and
+        ``fn rotate_activation`` (the ConvRot rotation the first page imports).
+
+Precision.  The pages fix fp32 for the stored scales, the decode product, the
+quantizer's divisions and the epilogue; the oracle does those steps in numpy
+float32 (IEEE, round-to-nearest-even, no fused multiply-add).  Where the pages
+leave the precision open the oracle uses the readings listed in the design doc:
+
+  * rotation: the exact block product (fp64 here) rounded once to fp32;
+  * quantizer sums (ALS): fp32 products added in fp64 in k order, then fp32;
+  * int32 contraction: exact (fp64 BLAS is exact for these magnitudes, checked);
+  * int32 -> fp32 and fp32 -> bf16 conversions: round-to-nearest-even;
+  * a NaN decode product (an fp8 NaN scale byte) decodes to 0.
+
+Parity pins live in ``tests/test_oracle_*.py`` (closed forms, hand-worked
+values in ``tests/golden/``, library special cases, brute force on small
+tiles).  Parity unpinned: the optimality of ``FIXED_CODEBOOK`` and the quality
+gain of the ALS passes are taken from the page as given.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "FIXED_CODEBOOK", "uniform_codebook", "ALS_ITERS", "ROT_BLOCK", "GROUP",
+    "ACT_QMAX", "e4m3fn_to_f32", "f32_to_e4m3fn", "f32_to_bf16_bits",
+    "bf16_bits_to_f32", "hadamard", "rotate", "rotate_to_f32", "quant_act",
+    "rotate_quant_act", "pack_codes", "unpack_codes", "decode_w4",
+    "assign_codes", "grid_levels", "assign_grid", "quantize_w4_rotated",
+    "quantize_w4", "gemm_exact", "epilogue", "linear", "dequantize",
+]
+
+F32 = np.float32
+
+# [AT] FIXED_CODEBOOK: the sixteen sorted Lloyd-Max levels for a group-normalised
+# Gaussian, as printed, each converted to fp32 (round to nearest).
+FIXED_CODEBOOK = np.array(
+    [-0.980602, -0.794529, -0.638165, -0.500986, -0.377321, -0.263187, -0.155210, -0.050720,
+     0.052541, 0.156985, 0.265284, 0.379533, 0.502636, 0.638953, 0.794876, 0.980671],
+    dtype=np.float64).astype(F32)
+
+ALS_ITERS = 2     # [AT] _ALS_ITERS: two refinement passes of the group scale
+ROT_BLOCK = 256   # [AT] ConvRotW4A8Quantizer default rotation block
+GROUP = 16        # [AT] ConvRotW4A8Quantizer default group size
+ACT_QMAX = 127    # symmetric int8 activations (reading: act_qmax = 127)
+
+
+def uniform_codebook() -> np.ndarray:
+    """[AT] ConvRotW4A8Quantizer.attach_: when no codebook is given the levels
+    are the signed integers code - 8."""
+    return (np.arange(16, dtype=np.float64) - 8.0).astype(F32)
+
+
+# ----------------------------------------------------------------------------
+# number formats
+
+def e4m3fn_to_f32(b) -> np.ndarray:
+    """OCP fp8 E4M3FN byte -> fp32 (the ``torch.float8_e4m3fn`` storage the
+    [AT] group scales use).  Bias 7, 3 mantissa bits, subnormals m/8 * 2^-6,
+    no infinities, bytes 0x7F and 0xFF are NaN.  Exact in fp32."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    val = sign * mag
+    val = np.where((b & 0x7F) == 0x7F, np.nan, val)
+    return val.astype(F32)
+
+
+def f32_to_e4m3fn(x) -> np.ndarray:
+    """fp32 -> E4M3FN byte with round-to-nearest-even on the mantissa, keeping
+    subnormals ([AT] ``_quantize_rotated_rows`` converts s_rel with
+    ``.to(torch.float8_e4m3fn)``).  Magnitudes above 464 (half-way past the
+    largest finite value 448) and NaN give the NaN byte, as torch does."""
+    v = np.asarray(x, dtype=F32).astype(np.float64)   # exact
+    sign = np.where(np.signbit(v), 0x80, 0x00).astype(np.int64)
+    a = np.abs(v)
+    bad = np.isnan(a) | (a > 464.0)
+    a = np.where(bad, 1.0, a)
+    # subnormal range: a multiple of 2^-9; the quotient is exact, rint is RNE.
+    # A result of 8 is the byte 0x08, the smallest normal, as it should be.
+    sub_m = np.rint(a / 2.0 ** -9).astype(np.int64)
+    # normal range: a = (1 + f) * 2^e with f in [0, 1); round f to eighths (RNE)
+    mant, ex = np.frexp(np.maximum(a, 2.0 ** -6))      # a = mant * 2^ex, mant in [0.5, 1)
+    e = ex.astype(np.int64) - 1
+    m = np.rint((2.0 * mant - 1.0) * 8.0).astype(np.int64)
+    carry = m == 8
+    e = np.where(carry, e + 1, e)
+    m = np.where(carry, 0, m)
+    normal = (e + 7) << 3 | m
+    mag = np.where(a < 2.0 ** -6, sub_m, normal)
+    assert np.all(bad | (mag < 0x7F)), "finite e4m3 range exceeded"
+    mag = np.where(bad, 0x7F, mag)
+    return (sign | mag).astype(np.uint8)
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """fp32 -> bfloat16 bit pattern, round to nearest even (the output cast in
+    [AT] ``w4a8_gemv_kernel``'s store); NaN maps to a quiet NaN."""
+    u = np.asarray(x, dtype=F32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    isnan = np.isnan(np.asarray(x, dtype=F32))
+    rounded = np.where(isnan, (u >> 16) | 0x40, rounded)
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(F32)
+
+
+# ----------------------------------------------------------------------------
+# rotation  ([H3] fn hadamard, fn rotate_activation)
+
+def hadamard(size: int = ROT_BLOCK) -> np.ndarray:
+    """[H3] fn hadamard: Kronecker powers of the symmetric 4x4 regular Hadamard
+    matrix (all ones except -1 on the anti-diagonal) grown until the size is
+    reached (a size that is not a power of 4 is an error), divided by sqrt(size).
+    Returned in fp64 (entries +-1/16 for size 256, exact)."""
+    h4 = np.array([[1, 1, 1, -1], [1, 1, -1, 1], [1, -1, 1, 1], [-1, 1, 1, 1]], dtype=np.float64)
+    h, n = h4, 4
+    while n < size:
+        h = np.kron(h, h4)
+        n *= 4
+    if n != size:
+        raise ValueError(f"rotation size {size} is not a power of 4")
+    return h / np.sqrt(size)
+
+
+def rotate(x, block: int = ROT_BLOCK) -> np.ndarray:
+    """[H3] fn rotate_activation: the last dimension is cut into consecutive
+    blocks of ``block`` columns and each block (a row vector) is multiplied by
+    the normalised Hadamard matrix.  Computed in fp64 and returned in fp64;
+    the matrix is symmetric and its own inverse ([AT] dequantize_w4a8 relies
+    on applying it twice)."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.shape[-1] % block:
+        raise ValueError(f"block {block} does not divide {x.shape}")
+    h = hadamard(block)
+    y = x.reshape(-1, block) @ h
+    return y.reshape(x.shape)
+
+
+def rotate_to_f32(x, block: int = ROT_BLOCK) -> np.ndarray:
+    """The rotated value rounded once to fp32 (reading: no intermediate
+    rounding; used for bf16 activations and for fp32 weights)."""
+    return rotate(x, block).astype(F32)
+
+
+# ----------------------------------------------------------------------------
+# activation quantisation  ([AT] w4a8_act_quant_kernel)
+
+def quant_act(v, qmax: int = ACT_QMAX):
+    """[AT] w4a8_act_quant_kernel, per row of fp32 values: amax = max |v|;
+    scale = amax / qmax in fp32 (1.0 for an all-zero row); q = v / scale in
+    fp32, rounded half-to-even and clamped to [-qmax, qmax].  Returns
+    (int8 [M, K], fp32 [M])."""
+    v = np.asarray(v, dtype=F32)
+    amax = np.abs(v).max(axis=1)
+    scale = np.where(amax > 0, amax / F32(qmax), F32(1.0)).astype(F32)
+    q = np.rint((v / scale[:, None]).astype(F32))
+    q = np.clip(q, -qmax, qmax)
+    return q.astype(np.int8), scale
+
+
+def rotate_quant_act(x, block: int = ROT_BLOCK, qmax: int = ACT_QMAX):
+    """Rotate each row (exact, one rounding to fp32) and quantise it to int8
+    with one fp32 scale per row ([AT] ConvRotW4A8Quantizer.prepare_act)."""
+    return quant_act(rotate_to_f32(x, block), qmax)
+
+
+# ----------------------------------------------------------------------------
+# storage: pack / unpack / decode  ([AT] module docstring, _pack_codes,
+# _unpack_codes, unpack_w4a8_eager, W4A8_SAT)
+
+def pack_codes(codes) -> np.ndarray:
+    """[AT] _pack_codes: codes [N, K] in 0..15 -> bytes [N, K/2]; column 2j
+    goes to the low nibble of byte j and column 2j+1 to the high nibble."""
+    c = np.asarray(codes).astype(np.int64)
+    return ((c[:, 0::2] & 0xF) | ((c[:, 1::2] & 0xF) << 4)).astype(np.uint8)
+
+
+def unpack_codes(packed) -> np.ndarray:
+    """[AT] _unpack_codes: the inverse of pack_codes."""
+    b = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    n, kh = b.shape
+    codes = np.empty((n, 2 * kh), dtype=np.int64)
+    codes[:, 0::2] = b & 0xF
+    codes[:, 1::2] = (b >> 4) & 0xF
+    return codes
+
+
+def decode_w4(packed, srel_u8, codebook, group: int = GROUP) -> np.ndarray:
+    """[AT] module docstring + unpack_w4a8_eager with W4A8_SAT: the int8 grid
+    value of weight (n, k) is codebook[code] * e4m3(srel[n, k // group]) in
+    fp32, rounded half-to-even and saturated to [-128, 127].  A NaN product
+    (scale byte 0x7F/0xFF) decodes to 0, as a saturating float->int8
+    conversion does.  Returns int8 [N, K]."""
+    codes = unpack_codes(packed)
+    n, k = codes.shape
+    cb = np.asarray(codebook, dtype=F32)
+    s = e4m3fn_to_f32(srel_u8)
+    assert s.shape == (n, k // group)
+    prod = cb[codes] * np.repeat(s, group, axis=1)          # fp32 product
+    r = np.rint(prod)
+    r = np.where(np.isnan(r), 0.0, r)
+    return np.clip(r, -128, 127).astype(np.int8)
+
+
+# ----------------------------------------------------------------------------
+# weight quantiser  ([AT] _assign_codes, grid_levels, _assign_grid,
+# _quantize_rotated_rows, quantize_w4a8_rotated)
+
+def _nearest_of_sorted(target, lv_lo, lv_hi):
+    """Shared tie rule of [AT] _assign_codes / _assign_grid given the two
+    candidate levels: distances in fp32; the upper candidate only when it is
+    strictly closer."""
+    dlo = np.abs((target - lv_lo).astype(F32))
+    dhi = np.abs((target - lv_hi).astype(F32))
+    return dhi < dlo
+
+
+def assign_codes(normalized, codebook) -> np.ndarray:
+    """[AT] _assign_codes: left insertion point p of each value in the sorted
+    codebook, candidates p-1 and p clamped to 0..15, the upper one only if it
+    is strictly closer."""
+    cb = np.asarray(codebook, dtype=F32)
+    x = np.asarray(normalized, dtype=F32)
+    last = cb.size - 1
+    pos = np.searchsorted(cb, x, side="left")
+    lo = np.clip(pos - 1, 0, last)
+    hi = np.clip(pos, 0, last)
+    return np.where(_nearest_of_sorted(x, cb[lo], cb[hi]), hi, lo)
+
+
+def grid_levels(codebook, srel_u8) -> np.ndarray:
+    """[AT] grid_levels: per group, the int8-grid value of each level,
+    rint(codebook * e4m3(srel)) in fp32 clamped to [-127, 127].  [N, G, 16]."""
+    cb = np.asarray(codebook, dtype=F32)
+    s = e4m3fn_to_f32(srel_u8)
+    lv = np.rint(cb[None, None, :] * s[:, :, None])
+    return np.clip(lv, -127, 127).astype(F32)
+
+
+def assign_grid(target, levels) -> np.ndarray:
+    """[AT] _assign_grid (deterministic branch): per group, left insertion
+    point of each target among the 16 non-decreasing levels (the count of
+    levels below it), candidates p-1 and p clamped, the upper one only if
+    strictly closer.  target [N, G, g], levels [N, G, 16] -> codes [N, G, g]."""
+    t = np.asarray(target, dtype=F32)
+    lv = np.asarray(levels, dtype=F32)
+    last = lv.shape[-1] - 1
+    pos = (lv[:, :, None, :] < t[:, :, :, None]).sum(axis=-1)
+    lo = np.clip(pos - 1, 0, last)
+    hi = np.clip(pos, 0, last)
+    lv_lo = np.take_along_axis(lv, lo.reshape(lv.shape[0], lv.shape[1], -1), axis=2).reshape(t.shape)
+    lv_hi = np.take_along_axis(lv, hi.reshape(lv.shape[0], lv.shape[1], -1), axis=2).reshape(t.shape)
+    return np.where(_nearest_of_sorted(t, lv_lo, lv_hi), hi, lo)
+
+
+def _sum_k_f64(a):
+    """Sum over the last axis, adding fp32 terms in fp64 in index order, then
+    rounding once to fp32 (reading of the ALS sums)."""
+    acc = np.zeros(a.shape[:-1], dtype=np.float64)
+    for k in range(a.shape[-1]):
+        acc = acc + a[..., k].astype(np.float64)
+    return acc.astype(F32)
+
+
+def _quantize_rows(w_rot, codebook, group, internals=None):
+    """[AT] _quantize_rotated_rows on one chunk of rows of the rotated fp32
+    weight:
+      1. group scale gs = max |w| over the group, at least 1e-8;
+      2. codes = nearest codebook level of w / gs;
+      3. twice: gs = sum(w * cb[q]) / max(sum(cb[q]^2), 1e-8), at least 1e-8,
+         then re-assign the codes;
+      4. channel scale = max over the row of |cb[q] * gs| / 127, at least 1e-8;
+      5. relative group scale = e4m3(gs / channel scale);
+      6. final codes = nearest int8-grid level (grid_levels) of w / channel scale.
+    Returns (packed u8 [n, K/2], srel u8 [n, G], s_channel fp32 [n]).  When
+    ``internals`` is a dict it receives the intermediate arrays (for tests)."""
+    n, k = w_rot.shape
+    groups = k // group
+    tiny = F32(1e-8)
+    cb = np.asarray(codebook, dtype=F32)
+    gw = np.asarray(w_rot, dtype=F32).reshape(n, groups, group)
+    gs = np.maximum(np.abs(gw).max(axis=-1, keepdims=True), tiny)
+    q = assign_codes((gw / gs).astype(F32), cb)
+    if internals is not None:
+        internals["gs0"], internals["q0"] = gs.copy(), q.copy()
+    for it in range(ALS_ITERS):
+        lv = cb[q]
+        num = _sum_k_f64((gw * lv).astype(F32))[..., None]
+        den = np.maximum(_sum_k_f64((lv * lv).astype(F32))[..., None], tiny)
+        if internals is not None:
+            internals[f"q_used{it + 1}"] = q.copy()
+        gs = np.maximum((num / den).astype(F32), tiny)
+        q = assign_codes((gw / gs).astype(F32), cb)
+        if internals is not None:
+            internals[f"gs{it + 1}"], internals[f"q{it + 1}"] = gs.copy(), q.copy()
+    shifted = (cb[q] * gs).astype(F32)
+    s_channel = np.maximum((np.abs(shifted).max(axis=(1, 2)) / F32(127.0)).astype(F32), tiny)
+    srel = f32_to_e4m3fn((gs[..., 0] / s_channel[:, None]).astype(F32))
+    target = (gw / s_channel[:, None, None]).astype(F32)
+    codes = assign_grid(target, grid_levels(cb, srel))
+    if internals is not None:
+        internals.update(gw=gw, gs=gs, q=q, s_channel=s_channel, srel=srel, target=target, codes=codes)
+    return pack_codes(codes.reshape(n, k)), srel, s_channel.astype(F32)
+
+
+def quantize_w4_rotated(w_rot, codebook=None, group: int = GROUP, row_budget: int = 1 << 20):
+    """[AT] quantize_w4a8_rotated: K must be a multiple of 16 and of the group
+    (ValueError otherwise); rows are independent and are processed in chunks
+    (memory only).  Returns (packed u8 [N, K/2], srel u8 [N, K/group],
+    s_channel fp32 [N], codebook fp32 [16])."""
+    w_rot = np.asarray(w_rot, dtype=F32)
+    n, k = w_rot.shape
+    if k % group or k % 16:
+        raise ValueError(f"K={k} must be divisible by 16 and by group={group}")
+    cb = FIXED_CODEBOOK if codebook is None else np.asarray(codebook, dtype=F32)
+    block = max(1, row_budget // max(k, 1))
+    parts = [_quantize_rows(w_rot[r0:r0 + block], cb, group) for r0 in range(0, n, block)]
+    packed = np.concatenate([p[0] for p in parts], axis=0)
+    srel = np.concatenate([p[1] for p in parts], axis=0)
+    sch = np.concatenate([p[2] for p in parts], axis=0)
+    return packed, srel, sch, cb
+
+
+def quantize_w4(w, codebook=None, block: int = ROT_BLOCK, group: int = GROUP):
+    """[AT] ConvRotW4A8Quantizer.quantize_: rotate the fp32 weight (exact, one
+    rounding to fp32), then quantize_w4_rotated."""
+    return quantize_w4_rotated(rotate_to_f32(np.asarray(w, dtype=F32), block), codebook, group)
+
+
+# ----------------------------------------------------------------------------
+# contraction and epilogue  ([AT] _w4a8_linear_ste_op, w4a8_gemv_kernel)
+
+def gemm_exact(xq, w8) -> np.ndarray:
+    """acc[m, n] = sum_k xq[m, k] * w8[n, k] exactly ([AT] the int8 x int8 ->
+    int32 product of the prefill op and the GEMV's int32 multiply-accumulate).
+    Computed with fp64 BLAS: every product is below 2^14 in magnitude and every
+    partial sum below 2^53, so any summation order gives the exact integer.
+    Returns int64 [M, N]."""
+    a = np.asarray(xq, dtype=np.int8)
+    b = np.asarray(w8, dtype=np.int8)
+    k = a.shape[1]
+    assert b.shape[1] == k and 128 * 128 * k < 2 ** 53
+    acc = a.astype(np.float64) @ b.astype(np.float64).T
+    return acc.astype(np.int64)
+
+
+def epilogue(acc, xs, ws, bias=None, out: str = "bf16"):
+    """[AT] w4a8_gemv_kernel epilogue: y = fp32(acc) * (xs[m] * ws[n]) in fp32,
+    each product rounded separately, then + bias[n] in fp32 when given, then
+    the cast to the output type (bf16 round to nearest even).  ``out`` is
+    'bf16' (returns uint16 bit patterns), 'f32' or 'i32' (the raw int32
+    accumulator, no scaling)."""
+    acc = np.asarray(acc)
+    if out == "i32":
+        assert np.abs(acc).max(initial=0) < 2 ** 31
+        return acc.astype(np.int32)
+    accf = acc.astype(F32)                                  # int -> fp32, RNE
+    scale = (np.asarray(xs, dtype=F32)[:, None] * np.asarray(ws, dtype=F32)[None, :]).astype(F32)
+    y = (accf * scale).astype(F32)
+    if bias is not None:
+        y = (y + np.asarray(bias, dtype=F32)[None, :]).astype(F32)
+    if out == "f32":
+        return y
+    if out == "bf16":
+        return f32_to_bf16_bits(y)
+    raise ValueError(out)
+
+
+def linear(x, packed, srel_u8, s_channel, codebook, bias=None, out: str = "bf16",
+           block: int = ROT_BLOCK, group: int = GROUP, qmax: int = ACT_QMAX):
+    """The whole layer on bf16-valued activations x [M, K]: rotate + per-token
+    quant, decode, exact contraction, epilogue.  Returns (y, xq, xs, w8)."""
+    xq, xs = rotate_quant_act(x, block, qmax)
+    w8 = decode_w4(packed, srel_u8, codebook, group)
+    return epilogue(gemm_exact(xq, w8), xs, s_channel, bias, out), xq, xs, w8
+
+
+def dequantize(packed, srel_u8, s_channel, codebook, block: int = ROT_BLOCK, group: int = GROUP):
+    """[AT] dequantize_w4a8: decoded grid times the channel scale, rotated back
+    to the original basis (the rotation is an involution).  fp64 [N, K]; a
+    quality reference, not a parity target."""
+    w8 = decode_w4(packed, srel_u8, codebook, group).astype(np.float64)
+    w_rot = w8 * np.asarray(s_channel, dtype=np.float64)[:, None]
+    return rotate(w_rot, block)
