@@ -1,0 +1,208 @@
+// rotate_quant_act: block-256 regular-Hadamard rotation of bf16 activation rows
+// followed by per-row symmetric int8 quantisation.
+//
+// Rotation (h3-rs 0.2.0 src/weights.rs, fn hadamard / fn rotate_activation): each
+// 256-column block of a row is multiplied by H4^(x4) / 16, where H4 is the 4x4
+// regular Hadamard matrix (ones, minus ones on the anti-diagonal).  H4 = J - 2R
+// (all-ones minus twice the reversal), so one radix-4 stage maps (a0..a3) to
+// out_i = (a0 + a1 + a2 + a3) - 2 a_(3-i); four stages, one per base-4 digit of
+// the column index, give the whole block.
+//
+// Precision: inputs are bf16 (8 significant bits).  The stages run in fp64, where
+// every partial sum of +-x terms is exact unless the block's exponent spread
+// exceeds ~37 binades, so the result equals the exact block product; it is rounded
+// once to fp32.  This is the value the quantiser sees.
+//
+// Quantisation (ai-toolkit convrot_w4a8_quant.py, w4a8_act_quant_kernel): amax =
+// max |v| over the row, scale = amax / qmax in fp32 (1.0 when amax is 0),
+// q = round_half_even(fp32(v / scale)) clamped to [-qmax, qmax].  fp32(v / scale)
+// is computed as fp32(v * fp64(1 / scale)): the fp64 product is within 2^-52
+// relative of v / scale, while a quotient of two fp32 numbers is never an fp32
+// rounding midpoint and sits at least 2^-49 (relative) away from one, so the
+// rounding to fp32 is the IEEE quotient's.
+//
+// Layout: a block of 256 threads is 16 "slots" of 16 lanes; a slot rotates one
+// 256-column block.  Lane j loads columns 16j..16j+15 (two 16-byte loads), runs
+// the two stages of the low digits in registers, exchanges the 16 x 16 fp64
+// intermediate through LDS (transpose), runs the two stages of the high digits,
+// and ends with outputs 16i + j (i = 0..15).  Rows with K <= 4096 share a block
+// (16 / (K/256) rows per block); longer rows take 16 columns-blocks per pass and
+// keep up to CH passes of rotated values in registers between the absmax and the
+// quantisation, or recompute them (CH == 0) for very long rows.
+#include "w4a8_device.hpp"
+
+namespace w4a8 {
+namespace {
+
+constexpr int RQ_THREADS = 256;
+constexpr int TSTRIDE = 17;   // padded row of the fp64 transpose buffer (bank spread)
+
+__device__ __forceinline__ void radix4(double& a0, double& a1, double& a2, double& a3) {
+    const double s = (a0 + a1) + (a2 + a3);
+    const double b0 = __builtin_fma(-2.0, a3, s), b1 = __builtin_fma(-2.0, a2, s);
+    const double b2 = __builtin_fma(-2.0, a1, s), b3 = __builtin_fma(-2.0, a0, s);
+    a0 = b0; a1 = b1; a2 = b2; a3 = b3;
+}
+
+// radix-16 over v[4*d1 + d0]: the stage of digit d0, then of digit d1
+__device__ __forceinline__ void radix16(double (&v)[16]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) radix4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) radix4(v[g], v[g + 4], v[g + 8], v[g + 12]);
+}
+
+// Rotate block `blk` of row `row`.  Every thread of the block must call this (it
+// synchronises); threads with ok == false contribute zeros.  On return r[i] holds
+// the rotated value of column 16*i + l16 of the block, rounded to fp32.
+__device__ __forceinline__ void rotate_block(const uint16_t* __restrict__ x, int64_t row, int K, int blk,
+                                             bool ok, int slot, int l16, double* tbuf, float (&r)[16]) {
+    double v[16];
+    if (ok) {
+        const uint4* src = reinterpret_cast<const uint4*>(x + row * K + (int64_t)blk * 256 + l16 * 16);
+        const uint4 p0 = src[0], p1 = src[1];
+        const uint32_t w[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[2 * i] = (double)__uint_as_float(w[i] << 16);
+            v[2 * i + 1] = (double)__uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = 0.0;
+    }
+    radix16(v);     // digits 0, 1 of the input column (inside the lane)
+    double* t = tbuf + slot * (16 * TSTRIDE);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t[l16 * TSTRIDE + i] = v[i];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = t[j * TSTRIDE + l16];
+    __syncthreads();
+    radix16(v);     // digits 2, 3 (the lane index of the first half)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = (float)(v[i] * 0.0625);
+}
+
+__device__ __forceinline__ float slot_max(float a) {
+    a = __builtin_fmaxf(a, __shfl_xor(a, 8, 16));
+    a = __builtin_fmaxf(a, __shfl_xor(a, 4, 16));
+    a = __builtin_fmaxf(a, __shfl_xor(a, 2, 16));
+    a = __builtin_fmaxf(a, __shfl_xor(a, 1, 16));
+    return a;
+}
+
+__device__ __forceinline__ int8_t quant1(float v, double inv, float qmaxf) {
+    float q = __builtin_rintf((float)((double)v * inv));
+    q = __builtin_fminf(__builtin_fmaxf(q, -qmaxf), qmaxf);
+    return (int8_t)(int32_t)q;
+}
+
+// Quantise one rotated block held as r[i] = column 16*i + l16 and store it.
+__device__ __forceinline__ void quant_store(const float (&r)[16], double inv, float qmaxf, bool ok,
+                                            int8_t* __restrict__ xq, int64_t row, int K, int blk,
+                                            int slot, int l16, uint8_t* qbuf) {
+    uint8_t* qb = qbuf + slot * 256;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) qb[16 * i + l16] = (uint8_t)quant1(r[i], inv, qmaxf);
+    __syncthreads();
+    const uint4 out = *reinterpret_cast<const uint4*>(qb + 16 * l16);
+    if (ok) *reinterpret_cast<uint4*>(xq + row * K + (int64_t)blk * 256 + 16 * l16) = out;
+    __syncthreads();
+}
+
+template <int CH>
+__global__ __launch_bounds__(RQ_THREADS) void rotate_quant_kernel(const uint16_t* __restrict__ x, int64_t M, int K,
+                                                                  int qmax, int8_t* __restrict__ xq,
+                                                                  float* __restrict__ xs) {
+    __shared__ double tbuf[16 * 16 * TSTRIDE];
+    __shared__ __attribute__((aligned(16))) uint8_t qbuf[16 * 256];
+    __shared__ float smax[16];
+
+    const int tid = threadIdx.x, slot = tid >> 4, l16 = tid & 15;
+    const int nb = K >> 8;
+    int rows_per_wg, row_local, blk0, nch;
+    if (nb <= 16) {
+        rows_per_wg = 16 / nb; row_local = slot / nb; blk0 = slot % nb; nch = 1;
+    } else {
+        rows_per_wg = 1; row_local = 0; blk0 = slot; nch = (nb + 15) >> 4;
+    }
+    const int64_t row = (int64_t)blockIdx.x * rows_per_wg + row_local;
+    const bool row_ok = row_local < rows_per_wg && row < M;
+    const float qmaxf = (float)qmax;
+
+    constexpr int KEEP = CH > 0 ? CH : 1;
+    float keep[KEEP][16];
+    float amax = 0.0f;
+    if (CH > 0) {
+#pragma unroll
+        for (int c = 0; c < KEEP; ++c) {
+            if (c < nch) {
+                const int blk = blk0 + 16 * c;
+                rotate_block(x, row, K, blk, row_ok && blk < nb, slot, l16, tbuf, keep[c]);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(keep[c][i]));
+            }
+        }
+    } else {
+        for (int c = 0; c < nch; ++c) {
+            const int blk = blk0 + 16 * c;
+            float r[16];
+            rotate_block(x, row, K, blk, row_ok && blk < nb, slot, l16, tbuf, r);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(r[i]));
+        }
+    }
+
+    // row absmax: over the slot's 16 lanes, then over the row's slots
+    amax = slot_max(amax);
+    if (l16 == 0) smax[slot] = amax;
+    __syncthreads();
+    float rmax = 0.0f;
+    if (nb <= 16) {
+        for (int s = row_local * nb; s < row_local * nb + nb && s < 16; ++s) rmax = __builtin_fmaxf(rmax, smax[s]);
+    } else {
+        for (int s = 0; s < 16; ++s) rmax = __builtin_fmaxf(rmax, smax[s]);
+    }
+    const float scale = rmax > 0.0f ? rmax / qmaxf : 1.0f;   // IEEE fp32 division
+    const double inv = 1.0 / (double)scale;
+    if (row_ok && l16 == 0 && blk0 == 0) xs[row] = scale;
+
+    if (CH > 0) {
+#pragma unroll
+        for (int c = 0; c < KEEP; ++c) {
+            if (c < nch) {
+                const int blk = blk0 + 16 * c;
+                quant_store(keep[c], inv, qmaxf, row_ok && blk < nb, xq, row, K, blk, slot, l16, qbuf);
+            }
+        }
+    } else {
+        for (int c = 0; c < nch; ++c) {
+            const int blk = blk0 + 16 * c;
+            float r[16];
+            rotate_block(x, row, K, blk, row_ok && blk < nb, slot, l16, tbuf, r);
+            quant_store(r, inv, qmaxf, row_ok && blk < nb, xq, row, K, blk, slot, l16, qbuf);
+        }
+    }
+}
+
+}  // namespace
+
+// Rows per block and the register-kept pass count follow K; grid = ceil(M / rows).
+hipError_t launch_rotate_quant(const uint16_t* x, int64_t M, int K, int qmax, int8_t* xq, float* xs,
+                               hipStream_t stream) {
+    (void)hipGetLastError();   // clear a stale error so the check below is about this launch
+    const int nb = K >> 8;
+    const int rows_per_wg = nb <= 16 ? 16 / nb : 1;
+    const int nch = nb <= 16 ? 1 : (nb + 15) / 16;
+    const int64_t grid = (M + rows_per_wg - 1) / rows_per_wg;
+    const dim3 g((unsigned)grid), b(RQ_THREADS);
+    if (nch <= 1) hipLaunchKernelGGL(rotate_quant_kernel<1>, g, b, 0, stream, x, M, K, qmax, xq, xs);
+    else if (nch <= 2) hipLaunchKernelGGL(rotate_quant_kernel<2>, g, b, 0, stream, x, M, K, qmax, xq, xs);
+    else if (nch <= 4) hipLaunchKernelGGL(rotate_quant_kernel<4>, g, b, 0, stream, x, M, K, qmax, xq, xs);
+    else if (nch <= 8) hipLaunchKernelGGL(rotate_quant_kernel<8>, g, b, 0, stream, x, M, K, qmax, xq, xs);
+    else hipLaunchKernelGGL(rotate_quant_kernel<0>, g, b, 0, stream, x, M, K, qmax, xq, xs);
+    return hipGetLastError();
+}
+
+}  // namespace w4a8

@@ -1,0 +1,131 @@
+// C ABI entry points of libw4a8 (declared in include/w4a8.h).
+//
+// Every entry point validates its arguments on the host first -- without any HIP
+// call -- so a rejected call enqueues and writes nothing.  Then it launches on the
+// caller's stream and reports a launch failure as W4A8_ERR_HIP.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/w4a8.h"
+
+namespace w4a8 {
+hipError_t launch_rotate_quant(const uint16_t* x, int64_t M, int K, int qmax, int8_t* xq, float* xs,
+                               hipStream_t stream);
+hipError_t launch_decode(const uint8_t* qp, const uint8_t* srel, const float* codebook, int64_t N, int K,
+                         int8_t* w8, hipStream_t stream);
+hipError_t launch_gemv(const int8_t* xq, const float* xs, int M, const uint8_t* qp, const uint8_t* srel,
+                       const float* codebook, const float* ws, const float* bias, int N, int K, int out_type,
+                       void* out, hipStream_t stream);
+hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, const uint8_t* qp, const uint8_t* srel,
+                       const float* codebook, const float* ws, const float* bias, int N, int K, int out_type,
+                       void* out, hipStream_t stream);
+}  // namespace w4a8
+
+namespace {
+
+// Largest M and N accepted: keeps row indices and tile counts in 32-bit range.
+constexpr int64_t MAX_ROWS = int64_t(1) << 30;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_k(int64_t K) {
+    if (K < 0) return W4A8_ERR_INVALID_ARG;
+    if (K < W4A8_ROT_BLOCK || K % W4A8_ROT_BLOCK != 0 || K > W4A8_MAX_K) return W4A8_ERR_SHAPE;
+    return W4A8_OK;
+}
+
+int check_n(int64_t N) {
+    if (N < 0) return W4A8_ERR_INVALID_ARG;
+    if (N < 1 || N > MAX_ROWS) return W4A8_ERR_SHAPE;
+    return W4A8_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP; }
+
+// Shared checks of w4a8_gemm / w4a8_gemv.
+int check_linear(const int8_t* xq, const float* xs, int64_t M, const uint8_t* qpacked, const uint8_t* srel,
+                 const float* codebook, const float* s_channel, const float* bias, int64_t N, int64_t K,
+                 int32_t group, int32_t out_type, const void* out) {
+    if (M < 0) return W4A8_ERR_INVALID_ARG;
+    if (M > MAX_ROWS) return W4A8_ERR_SHAPE;
+    int st = check_n(N);
+    if (st) return st;
+    if ((st = check_k(K))) return st;
+    if (out_type < W4A8_OUT_BF16 || out_type > W4A8_OUT_I32) return W4A8_ERR_INVALID_ARG;
+    if (group != W4A8_GROUP) return W4A8_ERR_UNSUPPORTED;
+    if (!qpacked || !srel || !codebook || !s_channel) return W4A8_ERR_INVALID_ARG;
+    if (M > 0 && (!xq || !xs || !out)) return W4A8_ERR_INVALID_ARG;
+    if (!aligned(qpacked, 16) || !aligned(srel, 16) || !aligned(codebook, 4) || !aligned(s_channel, 4) ||
+        !aligned(bias, 4))
+        return W4A8_ERR_ALIGN;
+    if (M > 0 && (!aligned(xq, 16) || !aligned(xs, 4) || !aligned(out, 16))) return W4A8_ERR_ALIGN;
+    return W4A8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rotate_quant_act(const void* x, int64_t M, int64_t K, int32_t rot_block, int32_t qmax, int8_t* xq, float* xs,
+                     void* stream) {
+    if (M < 0) return W4A8_ERR_INVALID_ARG;
+    if (M > MAX_ROWS) return W4A8_ERR_SHAPE;
+    int st = check_k(K);
+    if (st) return st;
+    if (rot_block != W4A8_ROT_BLOCK || qmax < 1 || qmax > 127) return W4A8_ERR_UNSUPPORTED;
+    if (M == 0) return W4A8_OK;
+    if (!x || !xq || !xs) return W4A8_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(xs, 4)) return W4A8_ERR_ALIGN;
+    return launched(w4a8::launch_rotate_quant(static_cast<const uint16_t*>(x), M, (int)K, qmax, xq, xs,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int decode_w4_to_int8(const uint8_t* qpacked, const uint8_t* srel, const float* codebook, int64_t N, int64_t K,
+                      int32_t group, int8_t* w8, void* stream) {
+    int st = check_n(N);
+    if (st) return st;
+    if ((st = check_k(K))) return st;
+    if (group != W4A8_GROUP) return W4A8_ERR_UNSUPPORTED;
+    if (!qpacked || !srel || !codebook || !w8) return W4A8_ERR_INVALID_ARG;
+    if (!aligned(qpacked, 16) || !aligned(srel, 16) || !aligned(codebook, 4) || !aligned(w8, 16))
+        return W4A8_ERR_ALIGN;
+    return launched(w4a8::launch_decode(qpacked, srel, codebook, N, (int)K, w8, static_cast<hipStream_t>(stream)));
+}
+
+int w4a8_gemm(const int8_t* xq, const float* xs, int64_t M, const uint8_t* qpacked, const uint8_t* srel,
+              const float* codebook, const float* s_channel, const float* bias, int64_t N, int64_t K, int32_t group,
+              int32_t out_type, void* out, void* stream) {
+    int st = check_linear(xq, xs, M, qpacked, srel, codebook, s_channel, bias, N, K, group, out_type, out);
+    if (st) return st;
+    if (((M + 255) / 256) * ((N + 127) / 128) > INT32_MAX) return W4A8_ERR_SHAPE;   // output tile count
+    if (M == 0) return W4A8_OK;
+    return launched(w4a8::launch_gemm(xq, xs, (int)M, qpacked, srel, codebook, s_channel, bias, (int)N, (int)K,
+                                      out_type, out, static_cast<hipStream_t>(stream)));
+}
+
+int w4a8_gemv(const int8_t* xq, const float* xs, int64_t M, const uint8_t* qpacked, const uint8_t* srel,
+              const float* codebook, const float* s_channel, const float* bias, int64_t N, int64_t K, int32_t group,
+              int32_t out_type, void* out, void* stream) {
+    int st = check_linear(xq, xs, M, qpacked, srel, codebook, s_channel, bias, N, K, group, out_type, out);
+    if (st) return st;
+    if (M > W4A8_GEMV_MAX_M) return W4A8_ERR_UNSUPPORTED;
+    if (M == 0) return W4A8_OK;
+    return launched(w4a8::launch_gemv(xq, xs, (int)M, qpacked, srel, codebook, s_channel, bias, (int)N, (int)K,
+                                      out_type, out, static_cast<hipStream_t>(stream)));
+}
+
+const char* w4a8_status_string(int status) {
+    switch (status) {
+        case W4A8_OK: return "W4A8_OK";
+        case W4A8_ERR_INVALID_ARG: return "W4A8_ERR_INVALID_ARG";
+        case W4A8_ERR_SHAPE: return "W4A8_ERR_SHAPE";
+        case W4A8_ERR_ALIGN: return "W4A8_ERR_ALIGN";
+        case W4A8_ERR_UNSUPPORTED: return "W4A8_ERR_UNSUPPORTED";
+        case W4A8_ERR_HIP: return "W4A8_ERR_HIP";
+        default: return "W4A8_ERR_UNKNOWN";
+    }
+}
+
+int w4a8_abi_version(void) { return 1; }
+
+}  // extern "C"

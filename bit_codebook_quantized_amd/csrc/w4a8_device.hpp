@@ -1,0 +1,101 @@
+// Device helpers shared by the W4A8 kernels (gfx950, wave64).
+//
+// Weight decode (ai-toolkit convrot_w4a8_quant.py, module docstring storage
+// contract, unpack_w4a8_eager with W4A8_SAT): the int8 grid value of a weight is
+// saturate_[-128,127](round_half_even(codebook[code] * e4m3(s_rel))) with the
+// product in fp32.  A layer has 256 possible scale bytes and 16 codes, so every
+// kernel that decodes first builds the 256 x 16 table of int8 levels in LDS
+// (4 KiB) and then turns packed nibbles into int8 with byte permutes
+// (v_perm_b32) against the 16-byte table row of the group's scale byte.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a8 {
+
+// OCP fp8 E4M3FN byte -> fp32, exact: bias 7, 3 mantissa bits, subnormals
+// m * 2^-9, no infinities, 0x7F / 0xFF are NaN.
+__device__ __forceinline__ float e4m3fn_to_f32(uint32_t b) {
+    const uint32_t sign = (b & 0x80u) << 24;
+    const uint32_t e = (b >> 3) & 0xFu;
+    const uint32_t m = b & 7u;
+    if ((b & 0x7Fu) == 0x7Fu) return __uint_as_float(0x7FC00000u | sign);
+    if (e == 0) return __uint_as_float(__float_as_uint((float)m * 0x1p-9f) | sign);
+    return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+}
+
+// One int8-grid level: fp32 product, round half to even, saturate; NaN -> 0.
+__device__ __forceinline__ uint32_t grid_level(float level, float scale) {
+    const float p = __fmul_rn(level, scale);
+    if (p != p) return 0u;
+    float r = __builtin_rintf(p);
+    r = __builtin_fminf(__builtin_fmaxf(r, -128.0f), 127.0f);
+    return (uint32_t)((int32_t)r) & 0xFFu;
+}
+
+// Fill the LDS level table: lut[4*b + q] holds the levels of codes 4q..4q+3 for
+// scale byte b, one byte each (code 4q in the low byte).  All threads of the
+// block take part; the caller synchronises afterwards.
+__device__ __forceinline__ void build_level_table(uint32_t* lut, const float* __restrict__ codebook,
+                                                  int tid, int nthreads) {
+    for (int i = tid; i < 1024; i += nthreads) {
+        const int b = i >> 2, q = i & 3;
+        const float s = e4m3fn_to_f32((uint32_t)b);
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w |= grid_level(codebook[4 * q + j], s) << (8 * j);
+        lut[i] = w;
+    }
+}
+
+// Byte permute: result byte i = byte sel_i of the 8-byte value {hi:lo}
+// (selectors 0..3 pick lo, 4..7 pick hi).
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Decode the 8 codes of one packed dword (byte i = code 2i | code 2i+1 << 4)
+// against the 16-level row t = {L0..3, L4..7, L8..11, L12..15}.
+// Returns the 8 int8 levels in natural column order: .x = k0..k3, .y = k4..k7.
+__device__ __forceinline__ uint2 decode8(uint32_t x, uint4 t) {
+    const uint32_t se = x & 0x07070707u;           // even codes, low 3 bits
+    const uint32_t so = (x >> 4) & 0x07070707u;    // odd codes, low 3 bits
+    const uint32_t lo_e = perm(t.y, t.x, se), hi_e = perm(t.w, t.z, se);
+    const uint32_t lo_o = perm(t.y, t.x, so), hi_o = perm(t.w, t.z, so);
+    // bit 3 of each code picks the upper half of the table: selector i or i + 4
+    const uint32_t me = ((x >> 1) & 0x04040404u) | 0x03020100u;
+    const uint32_t mo = ((x >> 5) & 0x04040404u) | 0x03020100u;
+    const uint32_t re = perm(hi_e, lo_e, me);      // columns 0, 2, 4, 6
+    const uint32_t ro = perm(hi_o, lo_o, mo);      // columns 1, 3, 5, 7
+    uint2 r;
+    r.x = perm(ro, re, 0x05010400u);
+    r.y = perm(ro, re, 0x07030602u);
+    return r;
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Epilogue of one output: fp32(acc) * (xs * ws) [+ bias], each op rounded on its own.
+__device__ __forceinline__ float epilogue_f32(int32_t acc, float xs, float ws, const float* bias, int n) {
+    float y = __fmul_rn((float)acc, __fmul_rn(xs, ws));
+    if (bias) y = __fadd_rn(y, bias[n]);
+    return y;
+}
+
+__device__ __forceinline__ void store_out(void* out, int out_type, int64_t idx, int32_t acc, float y) {
+    if (out_type == 0) {
+        reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16(y);
+    } else if (out_type == 1) {
+        reinterpret_cast<float*>(out)[idx] = y;
+    } else {
+        reinterpret_cast<int32_t*>(out)[idx] = acc;
+    }
+}
+
+}  // namespace w4a8

@@ -1,0 +1,198 @@
+"""Python binding of libw4a8 (the C ABI in include/w4a8.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libw4a8.so.  PyTorch supplies device memory and the current stream.  There is
+no fallback: if the library is not built, or a tensor is not on the GPU, the
+call raises.
+
+    layer = W4A8Layer(qpacked, srel, codebook, s_channel, bias=None)   # device tensors
+    y = linear(x_bf16, layer)               # rotate+quant, then GEMV (M <= 8) or GEMM
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so")
+
+OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP = range(6)
+OUT_BF16, OUT_F32, OUT_I32 = 0, 1, 2
+ROT_BLOCK, GROUP, GEMV_MAX_M, MAX_K = 256, 16, 8, 131072
+_OUT_CODES = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32, torch.int32: OUT_I32}
+
+# Symbols declared in include/w4a8.h, with their ctypes signatures.
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+SIGNATURES = {
+    "rotate_quant_act": [_P, _I64, _I64, _I32, _I32, _P, _P, _P],
+    "decode_w4_to_int8": [_P, _P, _P, _I64, _I64, _I32, _P, _P],
+    "w4a8_gemm": [_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P],
+    "w4a8_gemv": [_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P],
+    "w4a8_status_string": [ctypes.c_int],
+    "w4a8_abi_version": [],
+}
+
+_lib = None
+
+
+class W4A8Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+
+
+class W4A8ArgumentError(W4A8Error, ValueError):
+    pass
+
+
+def load() -> ctypes.CDLL:
+    """Load libw4a8.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built: run `python -m bit_codebook_quantized_amd.build` "
+                              "or __graft_entry__.build() first (there is no fallback path)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, args in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name == "w4a8_status_string" else ctypes.c_int
+        if lib.w4a8_abi_version() != 1:
+            raise ImportError("libw4a8.so ABI version mismatch")
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().w4a8_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status == OK:
+        return
+    if status == ERR_HIP:
+        raise W4A8Error(fn, status)
+    raise W4A8ArgumentError(fn, status)
+
+
+def call(fn: str, *args) -> int:
+    """Call a C entry point with raw arguments (pointers as ints); returns the status."""
+    return getattr(load(), fn)(*args)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+@dataclass
+class W4A8Layer:
+    """Device storage of one ConvRot W4A8 linear layer (see include/w4a8.h)."""
+    qpacked: torch.Tensor          # uint8 [N, K/2]
+    srel: torch.Tensor             # uint8 [N, K/16], fp8 e4m3fn bytes
+    codebook: torch.Tensor         # float32 [16]
+    s_channel: torch.Tensor        # float32 [N]
+    bias: Optional[torch.Tensor] = None   # float32 [N]
+
+    @property
+    def out_features(self) -> int:
+        return self.qpacked.shape[0]
+
+    @property
+    def in_features(self) -> int:
+        return self.qpacked.shape[1] * 2
+
+    @classmethod
+    def from_host(cls, qpacked, srel, codebook, s_channel, bias=None, device="cuda"):
+        t = lambda a, dt: torch.as_tensor(a).to(device=device, dtype=dt).contiguous()
+        return cls(t(qpacked, torch.uint8), t(srel, torch.uint8), t(codebook, torch.float32),
+                   t(s_channel, torch.float32), None if bias is None else t(bias, torch.float32))
+
+    def check(self) -> None:
+        n, kh = self.qpacked.shape
+        _dev(self.qpacked, torch.uint8, "qpacked")
+        _dev(self.srel, torch.uint8, "srel")
+        _dev(self.codebook, torch.float32, "codebook")
+        _dev(self.s_channel, torch.float32, "s_channel")
+        if tuple(self.srel.shape) != (n, 2 * kh // GROUP) or self.codebook.numel() != 16 \
+                or tuple(self.s_channel.shape) != (n,):
+            raise ValueError("W4A8Layer tensor shapes do not match")
+        if self.bias is not None:
+            _dev(self.bias, torch.float32, "bias")
+            if tuple(self.bias.shape) != (n,):
+                raise ValueError("bias must be [N]")
+
+
+def rotate_quant_act(x: torch.Tensor, qmax: int = 127, xq: torch.Tensor = None, xs: torch.Tensor = None):
+    """bf16 x [M, K] -> (int8 xq [M, K], float32 xs [M])."""
+    _dev(x, torch.bfloat16, "x")
+    m, k = x.shape
+    xq = torch.empty(m, k, dtype=torch.int8, device=x.device) if xq is None else xq
+    xs = torch.empty(m, dtype=torch.float32, device=x.device) if xs is None else xs
+    _check("rotate_quant_act", load().rotate_quant_act(x.data_ptr(), m, k, ROT_BLOCK, qmax, xq.data_ptr(),
+                                                      xs.data_ptr(), _stream(x)))
+    return xq, xs
+
+
+def decode_w4_to_int8(layer: W4A8Layer, out: torch.Tensor = None) -> torch.Tensor:
+    """The layer's int8 grid [N, K]."""
+    layer.check()
+    n, k = layer.out_features, layer.in_features
+    out = torch.empty(n, k, dtype=torch.int8, device=layer.qpacked.device) if out is None else out
+    _check("decode_w4_to_int8", load().decode_w4_to_int8(layer.qpacked.data_ptr(), layer.srel.data_ptr(),
+                                                         layer.codebook.data_ptr(), n, k, GROUP, out.data_ptr(),
+                                                         _stream(layer.qpacked)))
+    return out
+
+
+def _linear_call(fn: str, xq, xs, layer: W4A8Layer, out_dtype, out):
+    layer.check()
+    _dev(xq, torch.int8, "xq")
+    _dev(xs, torch.float32, "xs")
+    m, k = xq.shape
+    n = layer.out_features
+    if k != layer.in_features:
+        raise ValueError(f"xq has K={k}, layer has K={layer.in_features}")
+    if out_dtype not in _OUT_CODES:
+        raise ValueError(f"unsupported out_dtype {out_dtype}")
+    out = torch.empty(m, n, dtype=out_dtype, device=xq.device) if out is None else out
+    bias = layer.bias.data_ptr() if layer.bias is not None else None
+    st = getattr(load(), fn)(xq.data_ptr(), xs.data_ptr(), m, layer.qpacked.data_ptr(), layer.srel.data_ptr(),
+                             layer.codebook.data_ptr(), layer.s_channel.data_ptr(), bias, n, k, GROUP,
+                             _OUT_CODES[out_dtype], out.data_ptr(), _stream(xq))
+    _check(fn, st)
+    return out
+
+
+def w4a8_gemm(xq, xs, layer: W4A8Layer, out_dtype=torch.bfloat16, out=None):
+    return _linear_call("w4a8_gemm", xq, xs, layer, out_dtype, out)
+
+
+def w4a8_gemv(xq, xs, layer: W4A8Layer, out_dtype=torch.bfloat16, out=None):
+    return _linear_call("w4a8_gemv", xq, xs, layer, out_dtype, out)
+
+
+def linear(x: torch.Tensor, layer: W4A8Layer, out_dtype=torch.bfloat16) -> torch.Tensor:
+    """The whole layer for bf16 x [..., K]: rotate + quantise, then the GEMV for at
+    most 8 rows and the GEMM otherwise."""
+    shape = x.shape
+    x2 = x.reshape(-1, shape[-1]).contiguous()
+    xq, xs = rotate_quant_act(x2)
+    fn = w4a8_gemv if x2.shape[0] <= GEMV_MAX_M else w4a8_gemm
+    y = fn(xq, xs, layer, out_dtype)
+    return y.reshape(*shape[:-1], layer.out_features)

@@ -1,0 +1,145 @@
+/*
+ * w4a8.h -- C ABI of the ConvRot W4A8 codebook linear layer on AMD MI355X (gfx950).
+ *
+ * The layer (ai-toolkit, toolkit/util/convrot_w4a8_quant.py: module docstring and
+ * class ConvRotW4A8Quantizer) computes, for bf16 activations x [M, K]:
+ *
+ *   1. xr    = x rotated block-wise by the normalised regular Hadamard matrix of
+ *              size 256 (h3-rs 0.2.0, src/weights.rs: fn hadamard, fn rotate_activation);
+ *   2. xq,xs = per-token symmetric int8 quantisation of xr (ai-toolkit:
+ *              w4a8_act_quant_kernel);
+ *   3. w8    = the int8 grid decoded from packed 4-bit codebook indices and fp8-e4m3
+ *              group scales (ai-toolkit: storage contract, unpack_w4a8_eager, W4A8_SAT);
+ *   4. acc   = xq * w8^T exactly in int32;
+ *   5. y     = fp32(acc) * (xs[m] * s_channel[n]) [+ bias[n]] cast to the output type
+ *              (ai-toolkit: w4a8_gemv_kernel epilogue).
+ *
+ * Storage of one layer with N output channels and K input channels (K % 256 == 0):
+ *   qpacked   uint8 [N, K/2]   row-major; byte j of a row holds the code of column 2j in
+ *                              bits 0..3 and of column 2j+1 in bits 4..7 (codes 0..15).
+ *   srel      uint8 [N, K/16]  row-major OCP fp8 E4M3FN bytes, one per group of 16 columns.
+ *   codebook  float [16]       the 16 levels indexed by code (need not be sorted).
+ *   s_channel float [N]        per-output-channel fp32 scale.
+ *
+ * Conventions for every entry point:
+ *   - All buffers are DEVICE pointers owned by the caller, dense row-major, no strides.
+ *     The library allocates, frees and retains nothing and keeps no state between
+ *     calls; it never synchronises the stream.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously on it; concurrent calls on different streams are independent.
+ *   - Arguments are validated on the host before anything is launched; a call that
+ *     returns an error has enqueued nothing and written nothing.
+ *   - Return value: W4A8_OK (0) or one of the W4A8_ERR_* codes below.  No exception
+ *     crosses the ABI.  w4a8_status_string() names a code.
+ *   - Alignment: x, xq, qpacked, srel, w8 and out must be 16-byte aligned; xs,
+ *     codebook, s_channel and bias 4-byte aligned.
+ *   - Sizes: M >= 0 (M == 0 is a valid call that does nothing), N >= 1,
+ *     256 <= K <= W4A8_MAX_K with K % 256 == 0 (the bound keeps every int32
+ *     accumulator exact: 127 * 128 * K < 2^31).
+ */
+#ifndef W4A8_H
+#define W4A8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum w4a8_status {
+    W4A8_OK = 0,
+    W4A8_ERR_INVALID_ARG = 1,  /* NULL required pointer, negative size, unknown out_type */
+    W4A8_ERR_SHAPE = 2,        /* N < 1, K not a positive multiple of 256, K > W4A8_MAX_K */
+    W4A8_ERR_ALIGN = 3,        /* a pointer misses its required alignment */
+    W4A8_ERR_UNSUPPORTED = 4,  /* group != 16, rot_block != 256, qmax not in 1..127,
+                                  M > W4A8_GEMV_MAX_M for w4a8_gemv */
+    W4A8_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+};
+
+enum w4a8_out_type {
+    W4A8_OUT_BF16 = 0,  /* bfloat16, round to nearest even */
+    W4A8_OUT_F32 = 1,   /* float32 */
+    W4A8_OUT_I32 = 2    /* the raw int32 accumulator acc[m, n], no scaling or bias */
+};
+
+#define W4A8_ROT_BLOCK 256
+#define W4A8_GROUP 16
+#define W4A8_GEMV_MAX_M 8
+#define W4A8_MAX_K 131072
+
+/*
+ * rotate_quant_act -- steps 1 and 2 for M rows of activations.
+ *
+ * Follows h3-rs weights.rs fn rotate_activation (block rotation of the last dim by the
+ * Kronecker-power Hadamard of fn hadamard, divided by 16 for block 256) and ai-toolkit
+ * w4a8_act_quant_kernel (per-row absmax, scale = amax / qmax or 1.0 for a zero row,
+ * q = round_half_even(v / scale) clamped to [-qmax, qmax]).  The rotated value v is
+ * the exact block product rounded once to fp32; the division is the IEEE fp32 one.
+ *
+ *   x         in   bf16 bits [M, K]
+ *   M, K           rows and columns
+ *   rot_block      must be 256
+ *   qmax           1..127 (the layer uses 127)
+ *   xq        out  int8 [M, K]
+ *   xs        out  float [M], the per-row scales
+ */
+int rotate_quant_act(const void* x, int64_t M, int64_t K, int32_t rot_block, int32_t qmax,
+                     int8_t* xq, float* xs, void* stream);
+
+/*
+ * decode_w4_to_int8 -- step 3 materialised: the int8 grid of a whole layer.
+ *
+ * ai-toolkit module docstring and unpack_w4a8_eager with W4A8_SAT:
+ *   w8[n, k] = saturate_[-128,127](round_half_even(codebook[code(n, k)] * e4m3(srel[n, k/16])))
+ * with the product in fp32.  A NaN scale byte (0x7F, 0xFF) decodes to 0.
+ *
+ *   qpacked, srel, codebook   in   the layer storage (see above)
+ *   N, K                           output and input channels
+ *   group                          must be 16
+ *   w8                        out  int8 [N, K]
+ */
+int decode_w4_to_int8(const uint8_t* qpacked, const uint8_t* srel, const float* codebook,
+                      int64_t N, int64_t K, int32_t group, int8_t* w8, void* stream);
+
+/*
+ * w4a8_gemm -- steps 3 to 5 for any M (the prefill path of ai-toolkit
+ * _w4a8_linear_ste_op: decoded int8 grid x int8 activations -> int32 -> epilogue).
+ * The weight is decoded on chip; no int8 weight copy is written to memory.
+ *
+ *   xq, xs              in   int8 [M, K] and float [M] from rotate_quant_act
+ *   M                        rows (tokens), >= 0
+ *   qpacked, srel,      in   the layer storage
+ *   codebook, s_channel
+ *   bias                in   float [N] or NULL
+ *   N, K, group              sizes; group must be 16
+ *   out_type                 W4A8_OUT_BF16, W4A8_OUT_F32 or W4A8_OUT_I32
+ *   out                 out  [M, N] of the chosen type
+ */
+int w4a8_gemm(const int8_t* xq, const float* xs, int64_t M,
+              const uint8_t* qpacked, const uint8_t* srel, const float* codebook,
+              const float* s_channel, const float* bias, int64_t N, int64_t K, int32_t group,
+              int32_t out_type, void* out, void* stream);
+
+/*
+ * w4a8_gemv -- the same result as w4a8_gemm for 1 <= M <= W4A8_GEMV_MAX_M, computed by
+ * the decode-path kernel of ai-toolkit w4a8_gemv_kernel: packed codes, fp8 group
+ * scales and the codebook are read directly and multiply-accumulated in int32 with
+ * vector dot products (no matrix cores).  Output is bit-identical to w4a8_gemm.
+ * M > W4A8_GEMV_MAX_M returns W4A8_ERR_UNSUPPORTED.  Arguments as for w4a8_gemm.
+ */
+int w4a8_gemv(const int8_t* xq, const float* xs, int64_t M,
+              const uint8_t* qpacked, const uint8_t* srel, const float* codebook,
+              const float* s_channel, const float* bias, int64_t N, int64_t K, int32_t group,
+              int32_t out_type, void* out, void* stream);
+
+/* Name of a status code ("W4A8_OK", ...); never NULL. */
+const char* w4a8_status_string(int status);
+
+/* ABI version of this header (incremented on any signature change). */
+int w4a8_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A8_H */

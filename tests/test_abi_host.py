@@ -1,0 +1,114 @@
+"""Host-side tests of libw4a8: it loads, exports every function include/w4a8.h
+declares, and its argument validation rejects bad calls before touching the GPU
+(every call here fails validation, so nothing is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a8.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def w4a8():
+    from bit_codebook_quantized_amd import w4a8 as b
+    b.load()
+    return b
+
+
+def test_header_declares_the_four_operations():
+    names = _declared_functions()
+    for n in ("rotate_quant_act", "decode_w4_to_int8", "w4a8_gemm", "w4a8_gemv", "w4a8_status_string",
+              "w4a8_abi_version"):
+        assert n in names
+    assert len(names) == 6, names
+
+
+def test_library_exports_every_declared_symbol(w4a8):
+    lib = ctypes.CDLL(w4a8.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert set(_declared_functions()) == set(w4a8.SIGNATURES)
+
+
+def test_status_strings(w4a8):
+    assert [w4a8.status_string(i) for i in range(6)] == [
+        "W4A8_OK", "W4A8_ERR_INVALID_ARG", "W4A8_ERR_SHAPE", "W4A8_ERR_ALIGN", "W4A8_ERR_UNSUPPORTED",
+        "W4A8_ERR_HIP"]
+    assert w4a8.status_string(99) == "W4A8_ERR_UNKNOWN"
+    assert w4a8.load().w4a8_abi_version() == 1
+
+
+A = 1 << 20          # a 16-byte-aligned fake address (never dereferenced: validation fails first)
+U = A + 1            # misaligned
+
+
+def _lin(w4a8, fn, **kw):
+    a = dict(xq=A, xs=A, M=4, qp=A, srel=A, cb=A, sch=A, bias=None, N=64, K=256, group=16, out_type=0, out=A)
+    a.update(kw)
+    return w4a8.call(fn, a["xq"], a["xs"], a["M"], a["qp"], a["srel"], a["cb"], a["sch"], a["bias"], a["N"],
+                     a["K"], a["group"], a["out_type"], a["out"], None)
+
+
+@pytest.mark.parametrize("fn", ["w4a8_gemm", "w4a8_gemv"])
+def test_linear_validation(w4a8, fn):
+    assert _lin(w4a8, fn, M=-1) == w4a8.ERR_INVALID_ARG
+    assert _lin(w4a8, fn, N=0) == w4a8.ERR_SHAPE
+    assert _lin(w4a8, fn, N=-3) == w4a8.ERR_INVALID_ARG
+    for k in (0, 128, 300, 131072 + 256):
+        assert _lin(w4a8, fn, K=k) == w4a8.ERR_SHAPE, k
+    assert _lin(w4a8, fn, K=-256) == w4a8.ERR_INVALID_ARG
+    assert _lin(w4a8, fn, group=32) == w4a8.ERR_UNSUPPORTED
+    assert _lin(w4a8, fn, out_type=3) == w4a8.ERR_INVALID_ARG
+    for p in ("qp", "srel", "cb", "sch"):
+        assert _lin(w4a8, fn, **{p: None}) == w4a8.ERR_INVALID_ARG, p
+    for p in ("xq", "xs", "out"):
+        assert _lin(w4a8, fn, **{p: None}) == w4a8.ERR_INVALID_ARG, p
+        assert _lin(w4a8, fn, M=0, **{p: None, "qp": U}) == w4a8.ERR_ALIGN   # shapes ok, storage misaligned
+    for p in ("xq", "qp", "srel", "out"):
+        assert _lin(w4a8, fn, **{p: A + 8}) == w4a8.ERR_ALIGN, p
+    for p in ("xs", "cb", "sch", "bias"):
+        assert _lin(w4a8, fn, **{p: A + 2}) == w4a8.ERR_ALIGN, p
+
+
+def test_gemv_rejects_more_than_8_rows(w4a8):
+    assert _lin(w4a8, "w4a8_gemv", M=9) == w4a8.ERR_UNSUPPORTED
+    assert _lin(w4a8, "w4a8_gemv", M=9, qp=U) == w4a8.ERR_ALIGN      # validation order: storage first
+    assert _lin(w4a8, "w4a8_gemv", M=9, K=100) == w4a8.ERR_SHAPE
+    assert _lin(w4a8, "w4a8_gemv", M=9, group=8) == w4a8.ERR_UNSUPPORTED
+
+
+def test_rotate_quant_validation(w4a8):
+    c = lambda **kw: w4a8.call("rotate_quant_act", kw.get("x", A), kw.get("M", 4), kw.get("K", 256),
+                               kw.get("rot", 256), kw.get("qmax", 127), kw.get("xq", A), kw.get("xs", A), None)
+    assert c(M=-1) == w4a8.ERR_INVALID_ARG
+    assert c(K=255) == w4a8.ERR_SHAPE
+    assert c(rot=128) == w4a8.ERR_UNSUPPORTED
+    assert c(qmax=0) == w4a8.ERR_UNSUPPORTED and c(qmax=128) == w4a8.ERR_UNSUPPORTED
+    assert c(x=None) == w4a8.ERR_INVALID_ARG and c(xs=None) == w4a8.ERR_INVALID_ARG
+    assert c(x=A + 2) == w4a8.ERR_ALIGN and c(xq=A + 4) == w4a8.ERR_ALIGN and c(xs=A + 1) == w4a8.ERR_ALIGN
+    assert c(M=0, x=None, xq=None, xs=None) == w4a8.OK        # M == 0 is a no-op
+
+
+def test_decode_validation(w4a8):
+    c = lambda **kw: w4a8.call("decode_w4_to_int8", kw.get("qp", A), kw.get("srel", A), kw.get("cb", A),
+                               kw.get("N", 8), kw.get("K", 256), kw.get("group", 16), kw.get("w8", A), None)
+    assert c(N=0) == w4a8.ERR_SHAPE and c(K=16) == w4a8.ERR_SHAPE
+    assert c(group=64) == w4a8.ERR_UNSUPPORTED
+    assert c(w8=None) == w4a8.ERR_INVALID_ARG
+    assert c(w8=A + 4) == w4a8.ERR_ALIGN and c(srel=A + 8) == w4a8.ERR_ALIGN
+
+
+def test_binding_rejects_cpu_tensors(w4a8):
+    import torch
+    with pytest.raises(ValueError):
+        w4a8.rotate_quant_act(torch.zeros(2, 256, dtype=torch.bfloat16))
