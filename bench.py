@@ -1,0 +1,237 @@
+"""Benchmark of the ConvRot W4A8 codebook linear layer on one MI355X.
+
+Main line (the step): one W4A8 layer at M=2048, N=K=4096 -- rotate_quant_act on
+bf16 activations [2048, 4096] (N(0,1) with 1% of the columns x20) followed by
+w4a8_gemm (decode in LDS, int8 MFMA, fused epilogue, bf16 out).  value = layer
+TOPS = 2*M*N*K / wall time per step.  The same run also measures the decode
+GEMV sweep (M = 1, 2, 4, 8 on one N=K=4096 layer; each launch reads one of 64
+distinct weight copies, 605 MB > the 256 MB Infinity Cache, so weights come from
+HBM) and reports weight GB/s against the 8 TB/s HBM peak.
+
+Kernel durations come from HIP events recorded on the launch stream around every
+kernel inside the timed region.  Weights are random storage bytes whose scale
+bytes span the range a quantised Gaussian layer produces (the kernels' cost does
+not depend on the values); activations are seeded synthetic draws.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA, TOPS
+METRIC = "W4A8 linear TOPS (M=2048) and GEMV weight GB/s (M=1..8), % of roofline"
+
+
+def weight_bytes(n, k):
+    """Algorithmic bytes of one layer's storage: 4-bit codes, one fp8 scale per 16
+    weights, fp32 channel scales, the 64-byte codebook."""
+    return n * k // 2 + n * k // 16 + 4 * n + 64
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--gemv-launches", type=int, default=640)
+    p.add_argument("--sleep-cycles", type=float, default=4e7,
+                   help="GPU spin before a launch batch, so the host can queue the whole batch")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-gemv", action="store_true")
+    return p.parse_args()
+
+
+def make_layer(n, k, seed, device):
+    import torch
+    from bit_codebook_quantized_amd import synth
+    from bit_codebook_quantized_amd.w4a8 import W4A8Layer
+    from bit_codebook_quantized_amd.w4a8 import FIXED_CODEBOOK
+    packed, srel, sch = synth.random_layer_bytes(n, k, seed=seed, srel_lo=0x58, srel_hi=0x72)
+    cb = np.array(FIXED_CODEBOOK, np.float32)
+    return W4A8Layer.from_host(packed, srel, cb, sch, device=device), (packed, srel, sch, cb)
+
+
+def event_pairs(torch, n):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def mean_ms(pairs):
+    return float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+
+
+def bench_prefill(args, torch, B, device):
+    from bit_codebook_quantized_amd import synth
+    M, N, K = 2048, 4096, 4096
+    layer, host = make_layer(N, K, seed=synth.seed_for(2, 0, synth.ROLE_BYTES), device=device)
+    x_np = synth.activations(M, K, seed=synth.seed_for(2, 0, synth.ROLE_ACT), kind="outliers",
+                             outlier_seed=synth.seed_for(2, 0, synth.ROLE_OUTLIER))
+    x = torch.from_numpy(x_np).to(torch.bfloat16).to(device)
+    xq = torch.empty(M, K, dtype=torch.int8, device=device)
+    xs = torch.empty(M, dtype=torch.float32, device=device)
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=device)
+    rq_call = B.prepared_rotate_quant(x, xq, xs)
+    gemm_call = B.prepared_linear("w4a8_gemm", xq, xs, layer, out)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        rq_call()
+        if ev is not None:
+            ev[1].record()
+        gemm_call()
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    # step 0's events can include the host's first launch latency; the rest are queued
+    # behind the running GEMM, so they time the GPU alone
+    rq_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs[1:]]))
+    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs[1:]]))
+    ops = 2.0 * M * N * K
+    return dict(M=M, N=N, K=K, wall_s=wall, rq_ms=rq_ms, gemm_ms=gemm_ms, ops=ops, x_np=x_np, host=host,
+                rq_bytes=3 * M * K + 4 * M,
+                gemm_bytes=weight_bytes(N, K) + M * K + 4 * M + 2 * M * N)
+
+
+def timed_launches(torch, calls, n, sleep_cycles):
+    """Launch calls[i % len(calls)] n times with an event pair around each launch,
+    queued behind a GPU sleep long enough for the host to enqueue everything, so the
+    events time back-to-back GPU execution.  Returns the mean ms per launch."""
+    pairs = event_pairs(torch, n)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(sleep_cycles)
+    t0 = time.perf_counter()
+    for i in range(n):
+        pairs[i][0].record()
+        calls[i % len(calls)]()
+        pairs[i][1].record()
+    enqueue_s = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    return mean_ms(pairs), enqueue_s
+
+
+def bench_gemv(args, torch, B, device):
+    from bit_codebook_quantized_amd import synth
+    N = K = 4096
+    copies = 64
+    layers = [make_layer(N, K, seed=synth.seed_for(1, c, synth.ROLE_BYTES), device=device)[0] for c in range(copies)]
+    res = {}
+    sleep = int(args.sleep_cycles)
+    for m in (1, 2, 4, 8):
+        x = torch.from_numpy(synth.activations(m, K, seed=synth.seed_for(1, m, synth.ROLE_ACT))).to(
+            torch.bfloat16).to(device)
+        xq = torch.empty(m, K, dtype=torch.int8, device=device)
+        xs = torch.empty(m, dtype=torch.float32, device=device)
+        out = torch.empty(m, N, dtype=torch.bfloat16, device=device)
+        rq = [B.prepared_rotate_quant(x, xq, xs)]
+        cold = [B.prepared_linear("w4a8_gemv", xq, xs, layers[c], out) for c in range(copies)]
+        cold_ms, enq = timed_launches(torch, cold, args.gemv_launches, sleep)
+        warm_ms, _ = timed_launches(torch, cold[:1], 64, sleep // 4)
+        rq_ms, _ = timed_launches(torch, rq, 64, sleep // 4)
+        wb = weight_bytes(N, K)
+        res[str(m)] = dict(
+            gemv_us=round(cold_ms * 1e3, 3),
+            weight_GBps=round(wb / (cold_ms * 1e-3) / 1e9, 1),
+            frac=round(wb / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            total_GBps=round((wb + m * K + 4 * m + 2 * m * N) / (cold_ms * 1e-3) / 1e9, 1),
+            warm_cache_us=round(warm_ms * 1e3, 3),
+            warm_cache_weight_GBps=round(wb / (warm_ms * 1e-3) / 1e9, 1),
+            rotate_quant_us=round(rq_ms * 1e3, 3),
+            host_enqueue_us=round(enq / args.gemv_launches * 1e6, 2),
+        )
+    return res
+
+
+def cpu_baseline(pre, min_seconds=10.0):
+    """The oracle, untuned, on the host cores: the whole M=2048 layer step (rotate +
+    quantise, decode, exact contraction, epilogue), repeated until at least
+    ``min_seconds`` of CPU work have been timed (bounded at 30 repetitions)."""
+    import oracle as O
+    x = pre["x_np"]
+    packed, srel, sch, cb = pre["host"]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        xq, xs = O.rotate_quant_act(x)
+        w8 = O.decode_w4(packed, srel, cb)
+        acc = O.gemm_exact(xq, w8)
+        O.epilogue(acc, xs, sch, out="bf16")
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= 30:
+            break
+    ops = 2.0 * pre["M"] * pre["N"] * pre["K"] * reps
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": min(cores, threads), "kind": "oracle",
+            "sample": f"the full M=2048 N=K=4096 step (rotate+quant, decode, exact fp64-BLAS contraction, "
+                      f"epilogue) x{reps}, {dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the path shards along N; "
+              "multi-GPU runs are outside this build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from bit_codebook_quantized_amd import w4a8 as B
+    B.load()
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+
+    pre = bench_prefill(args, torch, B, device)
+    gemv = None if args.no_gemv else bench_gemv(args, torch, B, device)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(pre)
+
+    tops = pre["ops"] / pre["wall_s"] / 1e12
+    gemm_tops = pre["ops"] / (pre["gemm_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["wall_s"] * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "W4A8 layer prefill M=2048 N=4096 K=4096: rotate_quant_act + w4a8_gemm, "
+                               "bf16 activations N(0,1) with 41 outlier columns x20, bf16 output",
+                   "M": pre["M"], "N": pre["N"], "K": pre["K"], "rot_block": 256, "group": 16},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": None,
+                     "kernel": "w4a8_gemm", "kernel_us": round(pre["gemm_ms"] * 1e3, 3)},
+        "rotate_quant_act": {"us": round(pre["rq_ms"] * 1e3, 3),
+                             "GBps": round(pre["rq_bytes"] / (pre["rq_ms"] * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(pre["rq_bytes"] / (pre["rq_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "gemv": gemv,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -8,24 +8,67 @@
 // Weight traffic is 4 bits per code plus one scale byte per 16 codes (4.5 bit per
 // weight), which bounds the kernel by HBM bandwidth.
 //
-// Layout: a block of 256 threads = 4 waves; wave w owns R consecutive output rows
-// and its 64 lanes split K in 16-column chunks (one 8-byte load of codes, one scale
-// byte).  Per chunk a lane loads the M activation chunks once and reuses them for
-// its R rows.  The int32 partial sums stay in registers until the end of K and are
-// then summed across the wave once.  v_dot4_i32_i8 does four products per
-// instruction; the decode is done with byte permutes against the 16-level table
-// row of the group's scale byte (level table in LDS, built once per block).
+// Layout.  A block of 256 threads = 4 waves; wave w owns R consecutive output rows.
+// Its 64 lanes split K into 16-column groups (8 bytes of codes + 1 scale byte):
+// lane l takes groups l, l+64, l+128, ... so each load instruction reads 512
+// contiguous bytes of a row.  Groups are processed in batches of 4 per lane (4096
+// columns per wave); a batch's weight loads for all R rows are issued together and
+// the next batch is prefetched while the current one is decoded, so the bytes in
+// flight per compute unit cover HBM latency.  The first batch is issued before the
+// block builds its 256 x 16 level table in LDS and stages the int8 activations
+// (M x up to 32 KiB, reused by all R rows of all 4 waves) in LDS.
+//
+// Arithmetic per 16-column group and row: one LDS read of the 16-level table row
+// of the group's scale byte, two 8-code byte-permute decodes, and 4 v_dot4_i32_i8
+// per activation row.  The int32 partial sums of the R x M outputs stay in
+// registers for the whole of K and are combined across the wave once, by a
+// reduce-scatter (each halving step exchanges half the values), so a lane ends
+// with one fully summed output.
 #include "w4a8_device.hpp"
 
 namespace w4a8 {
 namespace {
 
 constexpr int GV_THREADS = 256;
+constexpr int GV_BATCH = 4;   // groups per lane per batch
 
-__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+constexpr int pow2_ceil(int v) { return v <= 1 ? 1 : 2 * pow2_ceil((v + 1) / 2); }
+constexpr int log2i(int v) { return v <= 1 ? 0 : 1 + log2i(v / 2); }
+
+// Columns of activations held in LDS at a time.
+__host__ __device__ constexpr int slab_cols(int mm) { return mm == 1 ? 32768 : mm == 2 ? 16384 : mm <= 4 ? 8192 : 4096; }
+
+template <int R>
+struct Batch {
+    uint2 q[GV_BATCH][R];
+    uint32_t s[GV_BATCH][R];
+};
+
+template <int R>
+__device__ __forceinline__ void load_batch(Batch<R>& b, const uint8_t* const (&qrow)[R], const uint8_t* const (&srow)[R],
+                                           int jbase, int nchunk) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    for (int u = 0; u < GV_BATCH; ++u) {
+        const int j = jbase + 64 * u;
+        if (j < nchunk) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                b.q[u][r] = *reinterpret_cast<const uint2*>(qrow[r] + (int64_t)j * 8);
+                b.s[u][r] = srow[r][j];
+            }
+        }
+    }
+}
+
+template <int MM>
+__device__ __forceinline__ void stage_acts(uint8_t* act, const int8_t* __restrict__ xq, int K, int k0, int cols) {
+    // MM rows x cols bytes of xq starting at column k0 -> act[m * cols_cap ...]
+    const int per_row = cols >> 4;   // uint4 per row
+    for (int i = threadIdx.x; i < MM * per_row; i += GV_THREADS) {
+        const int m = i / per_row, c = i - m * per_row;
+        *reinterpret_cast<uint4*>(act + m * slab_cols(MM) + c * 16) =
+            *reinterpret_cast<const uint4*>(xq + (int64_t)m * K + k0 + c * 16);
+    }
 }
 
 template <int MM, int R>
@@ -36,10 +79,11 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(const int8_t* __restri
                                                           const float* __restrict__ ws,
                                                           const float* __restrict__ bias, int N, int K,
                                                           int out_type, void* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) uint32_t lut[1024];
-    build_level_table(lut, codebook, threadIdx.x, GV_THREADS);
-    __syncthreads();
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint32_t* lut = reinterpret_cast<uint32_t*>(smem);
+    uint8_t* act = smem + 4096;
     const uint4* lut4 = reinterpret_cast<const uint4*>(lut);
+    constexpr int SLAB = slab_cols(MM);
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n0 = (blockIdx.x * (GV_THREADS / 64) + wave) * R;
@@ -54,47 +98,84 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(const int8_t* __restri
         srow[r] = srel + (int64_t)n * G;
     }
 
-    int32_t acc[R][MM];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int m = 0; m < MM; ++m) acc[r][m] = 0;
+    // first batch in flight before the table build and the activation staging
+    Batch<R> cur, nxt;
+    load_batch<R>(cur, qrow, srow, lane, nchunk);
+    const int cols0 = K < SLAB ? K : SLAB;
+    stage_acts<MM>(act, xq, K, 0, cols0);
+    build_level_table(lut, codebook, threadIdx.x, GV_THREADS);
+    __syncthreads();
 
-    for (int j = lane; j < nchunk; j += 64) {
-        uint4 a[MM];
+    int32_t acc[R * MM];
 #pragma unroll
-        for (int m = 0; m < MM; ++m) a[m] = *reinterpret_cast<const uint4*>(xq + (int64_t)m * K + j * 16);
+    for (int i = 0; i < R * MM; ++i) acc[i] = 0;
+
+    const int nbatch = (nchunk + 64 * GV_BATCH - 1) / (64 * GV_BATCH);
+    int slab_k0 = 0;
+    for (int b = 0; b < nbatch; ++b) {
+        const int kb = b * 64 * GV_BATCH * 16;          // first column of this batch
+        if (kb >= slab_k0 + SLAB) {                      // next slab of activations (uniform branch)
+            slab_k0 += SLAB;
+            __syncthreads();
+            const int cols = K - slab_k0 < SLAB ? K - slab_k0 : SLAB;
+            stage_acts<MM>(act, xq, K, slab_k0, cols);
+            __syncthreads();
+        }
+        if (b + 1 < nbatch) load_batch<R>(nxt, qrow, srow, lane + (b + 1) * 64 * GV_BATCH, nchunk);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint2 p = *reinterpret_cast<const uint2*>(qrow[r] + j * 8);
-            const uint4 t = lut4[srow[r][j]];
-            const uint2 d0 = decode8(p.x, t), d1 = decode8(p.y, t);
+        for (int u = 0; u < GV_BATCH; ++u) {
+            const int j = lane + (b * GV_BATCH + u) * 64;
+            if (j < nchunk) {
+                uint4 a[MM];
 #pragma unroll
-            for (int m = 0; m < MM; ++m) {
-                int32_t s = acc[r][m];
-                s = __builtin_amdgcn_sdot4((int)d0.x, (int)a[m].x, s, false);
-                s = __builtin_amdgcn_sdot4((int)d0.y, (int)a[m].y, s, false);
-                s = __builtin_amdgcn_sdot4((int)d1.x, (int)a[m].z, s, false);
-                s = __builtin_amdgcn_sdot4((int)d1.y, (int)a[m].w, s, false);
-                acc[r][m] = s;
+                for (int m = 0; m < MM; ++m)
+                    a[m] = *reinterpret_cast<const uint4*>(act + m * SLAB + (j * 16 - slab_k0));
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint4 t = lut4[cur.s[u][r]];
+                    const uint2 d0 = decode8(cur.q[u][r].x, t), d1 = decode8(cur.q[u][r].y, t);
+#pragma unroll
+                    for (int m = 0; m < MM; ++m) {
+                        int32_t s = acc[r * MM + m];
+                        s = __builtin_amdgcn_sdot4((int)d0.x, (int)a[m].x, s, false);
+                        s = __builtin_amdgcn_sdot4((int)d0.y, (int)a[m].y, s, false);
+                        s = __builtin_amdgcn_sdot4((int)d1.x, (int)a[m].z, s, false);
+                        s = __builtin_amdgcn_sdot4((int)d1.y, (int)a[m].w, s, false);
+                        acc[r * MM + m] = s;
+                    }
+                }
             }
         }
+        if (b + 1 < nbatch) cur = nxt;
     }
 
+    // reduce-scatter of the V = R*MM partial sums over the 64 lanes: after the
+    // halving steps lane l holds value l >> (6 - L) summed over its 2^(6-L) group
+    constexpr int V = R * MM, VP = pow2_ceil(V), L = log2i(VP);
+    static_assert(VP <= 64, "too many partial sums per wave");
+    int32_t v[VP];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int i = 0; i < VP; ++i) v[i] = i < V ? acc[i] : 0;
 #pragma unroll
-        for (int m = 0; m < MM; ++m) acc[r][m] = wave_sum(acc[r][m]);
+    for (int s = 0; s < L; ++s) {
+        const int o = 32 >> s, half = VP >> (s + 1);
+        const bool hi = (lane & o) != 0;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            const int32_t keep = hi ? v[i + half] : v[i];
+            const int32_t send = hi ? v[i] : v[i + half];
+            v[i] = keep + __shfl_xor(send, o, 64);
+        }
+    }
+#pragma unroll
+    for (int o = 32 >> L; o >= 1; o >>= 1) v[0] += __shfl_xor(v[0], o, 64);
 
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-#pragma unroll
-        for (int m = 0; m < MM; ++m) {
-            const int n = n0 + r;
-            if (lane == r * MM + m && n < N) {
-                const float y = epilogue_f32(acc[r][m], xs[m], ws[n], bias, n);
-                store_out(out, out_type, (int64_t)m * N + n, acc[r][m], y);
-            }
+    const int idx = lane >> (6 - L);
+    if ((lane & ((1 << (6 - L)) - 1)) == 0 && idx < V) {
+        const int r = idx / MM, m = idx - r * MM, n = n0 + r;
+        if (n < N) {
+            const float y = epilogue_f32(v[0], xs[m], ws[n], bias, n);
+            store_out(out, out_type, (int64_t)m * N + n, v[0], y);
         }
     }
 }
@@ -103,21 +184,21 @@ template <int MM>
 hipError_t launch_gemv_m(const int8_t* xq, const float* xs, const uint8_t* qp, const uint8_t* srel,
                          const float* codebook, const float* ws, const float* bias, int N, int K, int out_type,
                          void* out, hipStream_t stream) {
-    // rows per wave: enough waves to cover the 256 compute units several times
+    // rows per wave: as many as keep >= 2048 waves in the grid (8 per compute unit), at most 4
     const int waves_per_block = GV_THREADS / 64;
     int R = 4;
-    if ((N + 3) / 4 < 4 * 256) R = 2;
-    if ((N + 1) / 2 < 4 * 256) R = 1;
+    while (R > 1 && (N + R - 1) / R < 2048) R >>= 1;
     const int blocks = (N + waves_per_block * R - 1) / (waves_per_block * R);
+    const size_t lds = 4096 + (size_t)MM * slab_cols(MM);
     const dim3 g(blocks), b(GV_THREADS);
     if (R == 4)
-        hipLaunchKernelGGL((gemv_kernel<MM, 4>), g, b, 0, stream, xq, xs, qp, srel, codebook, ws, bias, N, K,
+        hipLaunchKernelGGL((gemv_kernel<MM, 4>), g, b, lds, stream, xq, xs, qp, srel, codebook, ws, bias, N, K,
                            out_type, out);
     else if (R == 2)
-        hipLaunchKernelGGL((gemv_kernel<MM, 2>), g, b, 0, stream, xq, xs, qp, srel, codebook, ws, bias, N, K,
+        hipLaunchKernelGGL((gemv_kernel<MM, 2>), g, b, lds, stream, xq, xs, qp, srel, codebook, ws, bias, N, K,
                            out_type, out);
     else
-        hipLaunchKernelGGL((gemv_kernel<MM, 1>), g, b, 0, stream, xq, xs, qp, srel, codebook, ws, bias, N, K,
+        hipLaunchKernelGGL((gemv_kernel<MM, 1>), g, b, lds, stream, xq, xs, qp, srel, codebook, ws, bias, N, K,
                            out_type, out);
     return hipGetLastError();
 }

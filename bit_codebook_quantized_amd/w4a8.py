@@ -25,6 +25,13 @@ OUT_BF16, OUT_F32, OUT_I32 = 0, 1, 2
 ROT_BLOCK, GROUP, GEMV_MAX_M, MAX_K = 256, 16, 8, 131072
 _OUT_CODES = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32, torch.int32: OUT_I32}
 
+# The default 16-level table (ai-toolkit convrot_w4a8_quant.py, FIXED_CODEBOOK):
+# Lloyd-Max levels for a group-normalised Gaussian, index = 4-bit code.
+FIXED_CODEBOOK = (
+    -0.980602, -0.794529, -0.638165, -0.500986, -0.377321, -0.263187, -0.155210, -0.050720,
+    0.052541, 0.156985, 0.265284, 0.379533, 0.502636, 0.638953, 0.794876, 0.980671,
+)
+
 # Symbols declared in include/w4a8.h, with their ctypes signatures.
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -90,6 +97,16 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _out(t, shape, dtype, device, name: str) -> torch.Tensor:
+    """A caller-provided output buffer must match exactly; None allocates one."""
+    if t is None:
+        return torch.empty(*shape, dtype=dtype, device=device)
+    _dev(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
 def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a CUDA (HIP) tensor")
@@ -142,8 +159,8 @@ def rotate_quant_act(x: torch.Tensor, qmax: int = 127, xq: torch.Tensor = None, 
     """bf16 x [M, K] -> (int8 xq [M, K], float32 xs [M])."""
     _dev(x, torch.bfloat16, "x")
     m, k = x.shape
-    xq = torch.empty(m, k, dtype=torch.int8, device=x.device) if xq is None else xq
-    xs = torch.empty(m, dtype=torch.float32, device=x.device) if xs is None else xs
+    xq = _out(xq, (m, k), torch.int8, x.device, "xq")
+    xs = _out(xs, (m,), torch.float32, x.device, "xs")
     _check("rotate_quant_act", load().rotate_quant_act(x.data_ptr(), m, k, ROT_BLOCK, qmax, xq.data_ptr(),
                                                       xs.data_ptr(), _stream(x)))
     return xq, xs
@@ -153,7 +170,7 @@ def decode_w4_to_int8(layer: W4A8Layer, out: torch.Tensor = None) -> torch.Tenso
     """The layer's int8 grid [N, K]."""
     layer.check()
     n, k = layer.out_features, layer.in_features
-    out = torch.empty(n, k, dtype=torch.int8, device=layer.qpacked.device) if out is None else out
+    out = _out(out, (n, k), torch.int8, layer.qpacked.device, "out")
     _check("decode_w4_to_int8", load().decode_w4_to_int8(layer.qpacked.data_ptr(), layer.srel.data_ptr(),
                                                          layer.codebook.data_ptr(), n, k, GROUP, out.data_ptr(),
                                                          _stream(layer.qpacked)))
@@ -166,11 +183,13 @@ def _linear_call(fn: str, xq, xs, layer: W4A8Layer, out_dtype, out):
     _dev(xs, torch.float32, "xs")
     m, k = xq.shape
     n = layer.out_features
+    if tuple(xs.shape) != (m,):
+        raise ValueError(f"xs must have shape ({m},)")
     if k != layer.in_features:
         raise ValueError(f"xq has K={k}, layer has K={layer.in_features}")
     if out_dtype not in _OUT_CODES:
         raise ValueError(f"unsupported out_dtype {out_dtype}")
-    out = torch.empty(m, n, dtype=out_dtype, device=xq.device) if out is None else out
+    out = _out(out, (m, n), out_dtype, xq.device, "out")
     bias = layer.bias.data_ptr() if layer.bias is not None else None
     st = getattr(load(), fn)(xq.data_ptr(), xs.data_ptr(), m, layer.qpacked.data_ptr(), layer.srel.data_ptr(),
                              layer.codebook.data_ptr(), layer.s_channel.data_ptr(), bias, n, k, GROUP,
@@ -196,3 +215,33 @@ def linear(x: torch.Tensor, layer: W4A8Layer, out_dtype=torch.bfloat16) -> torch
     fn = w4a8_gemv if x2.shape[0] <= GEMV_MAX_M else w4a8_gemm
     y = fn(xq, xs, layer, out_dtype)
     return y.reshape(*shape[:-1], layer.out_features)
+
+
+def prepare(fn: str, *tensors_and_args):
+    """A zero-argument callable that repeats one C entry-point call with the same
+    device buffers (pointers bound once; shapes are checked by the caller's first
+    regular call).  For launch loops and graph capture where per-call Python
+    overhead would dominate a microsecond kernel.  Tensors are passed as pointers;
+    the stream is the current stream at each call."""
+    c = getattr(load(), fn)
+    args = [a.data_ptr() if isinstance(a, torch.Tensor) else a for a in tensors_and_args]
+    dev = next(a for a in tensors_and_args if isinstance(a, torch.Tensor)).device
+
+    def run():
+        st = c(*args, torch.cuda.current_stream(dev).cuda_stream)
+        if st:
+            _check(fn, st)
+    return run
+
+
+def prepared_linear(fn: str, xq, xs, layer: W4A8Layer, out):
+    """prepare() for w4a8_gemm / w4a8_gemv with the checks of a regular call done once."""
+    _linear_call(fn, xq, xs, layer, out.dtype, out)     # validates shapes and runs once
+    bias = layer.bias.data_ptr() if layer.bias is not None else None
+    return prepare(fn, xq, xs, xq.shape[0], layer.qpacked, layer.srel, layer.codebook, layer.s_channel, bias,
+                   layer.out_features, layer.in_features, GROUP, _OUT_CODES[out.dtype], out)
+
+
+def prepared_rotate_quant(x, xq, xs, qmax: int = 127):
+    rotate_quant_act(x, qmax, xq, xs)                    # validates shapes and runs once
+    return prepare("rotate_quant_act", x, x.shape[0], x.shape[1], ROT_BLOCK, qmax, xq, xs)

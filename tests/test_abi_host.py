@@ -112,3 +112,10 @@ def test_binding_rejects_cpu_tensors(w4a8):
     import torch
     with pytest.raises(ValueError):
         w4a8.rotate_quant_act(torch.zeros(2, 256, dtype=torch.bfloat16))
+
+
+def test_binding_default_codebook_matches_the_page_table():
+    import numpy as np
+    import oracle as O
+    from bit_codebook_quantized_amd.w4a8 import FIXED_CODEBOOK
+    assert np.array_equal(np.array(FIXED_CODEBOOK, np.float32), O.FIXED_CODEBOOK)
