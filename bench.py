@@ -47,6 +47,8 @@ def parse():
                    help="GPU spin before a launch batch, so the host can queue the whole batch")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-gemv", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 256 MiB device-to-device copy 5 times (counter calibration)")
     return p.parse_args()
 
 
@@ -187,8 +189,43 @@ def cpu_baseline(pre, min_seconds=10.0):
                       f"epilogue) x{reps}, {dt:.1f} s wall"}
 
 
+GEMM_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bit_codebook_quantized_amd", "csrc",
+                        "gemm.hip")
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic_w4a8_gemm.json")
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch from the committed counter summary, if it was taken on
+    the kernel source as it is now (else None)."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(GEMM_SRC, "rb") as f:
+            src_hash = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("gemm_source_sha256") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+
+
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the path shards along N; "
               "multi-GPU runs are outside this build)", file=sys.stderr)
@@ -222,7 +259,7 @@ def main():
                                "bf16 activations N(0,1) with 41 outlier columns x20, bf16 output",
                    "M": pre["M"], "N": pre["N"], "K": pre["K"], "rot_block": 256, "group": 16},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": measured_traffic(),
                      "kernel": "w4a8_gemm", "kernel_us": round(pre["gemm_ms"] * 1e3, 3)},
         "rotate_quant_act": {"us": round(pre["rq_ms"] * 1e3, 3),
                              "GBps": round(pre["rq_bytes"] / (pre["rq_ms"] * 1e-3) / 1e9, 1),
