@@ -7,23 +7,35 @@
 // decoded int8 weight to memory and runs a library int8 GEMM on it, the weight is
 // decoded tile by tile into LDS here, so no int8 weight copy ever reaches HBM.
 //
-// Tiling: one block of 512 threads (8 waves) computes a BM x BN = 256 x 128 output
-// tile, stepping K by BK = 64.  Per step every thread loads 2 x 16 B of activation
-// rows and 8 B of packed codes (one row, one group of 16 columns) plus its scale
-// byte, decodes the codes with byte permutes against the LDS level table and
-// stores both tiles into LDS.  Tile rows are 64 B = four 16-byte chunks, and chunk c
-// of row r sits at position c ^ ((r >> 2) & 3): the writes (4 lanes per row) and the
-// fragment reads (16 rows at one chunk) both touch 16 distinct 16-byte bank groups.  The waves
-// form a 4 x 2 grid of 64 x 64 sub-tiles, each 4 x 4 v_mfma_i32_16x16x64_i8
-// accumulators (64 int32 registers per lane), so two waves fit on each SIMD: the
-// LDS only streams fragments near its peak with several waves per SIMD in flight.
-// Both MFMA operands are read as 16 consecutive k bytes per lane (lane % 16 = row,
-// lane / 16 = which 16-byte quarter of the K-step), so A and B agree on the k order
-// by construction.
+// Tiling.  A block of 512 threads (8 waves, two per SIMD) computes a 256 x 128 output
+// tile and steps K by 128 per iteration (two 64-deep MFMA half-steps).  Wave w owns the
+// 32 rows 32w..32w+31 and all 128 columns: 2 x 8 accumulators of
+// v_mfma_i32_16x16x64_i8.
+//  - Activations go straight from global memory into MFMA operand registers: no two
+//    waves share a row, so there is nothing to gain from LDS.  A lane loads 16
+//    consecutive k bytes of one row (16 rows x 64 B per load instruction).
+//  - The weight tile is decoded once per iteration into LDS and read by all 8 waves.
+//    Thread t loads 16 B of packed codes (two 16-column groups) of row t / 4 (16 rows x
+//    64 B per instruction, which the address unit serves at full rate), looks up the
+//    16 levels of each group's scale byte in the LDS level table, decodes with byte
+//    permutes and writes the 2 x 16 bytes where the MFMA fragment reads expect them.
+//  - Loads run ahead of use in register rings: activations two iterations, codes two
+//    and a half.
+//  - The decoded tile lives in three LDS buffers: iteration i multiplies buffer i % 3,
+//    while the tile of i + 2 is decoded into buffer (i + 2) % 3, one 16-column group in
+//    each half of the iteration, interleaved with the MFMAs.  The level-table rows a
+//    decode needs are read one half-iteration ahead.  One barrier per iteration, at its
+//    end.
+// MFMA operands are swapped (the weight fragment is the first operand) so that each lane
+// ends with 4 consecutive output columns of one row, stored as one vector.
 //
-// Tiles are mapped to blocks so that each of the 8 XCDs (blocks are dealt to
-// XCDs round robin) works on a contiguous range of tile ids, n fastest, which
-// keeps one activation row-panel and neighbouring weight panels in its L2.
+// Both operands of an MFMA hold, in lane l, 16 consecutive k of row (or column) l % 16
+// from 16-column group l / 16 of the half-step, so they agree on the k order by
+// construction, and one decoded group is exactly one lane's weight operand.
+//
+// Tiles are mapped to blocks so that each of the 8 XCDs (blocks are dealt to XCDs round
+// robin) works on a contiguous range of tile ids, n fastest, which keeps one activation
+// row panel in its L2 for all the weight panels.
 #include "w4a8_device.hpp"
 
 namespace w4a8 {
@@ -31,24 +43,26 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int GM_THREADS = 512;
-constexpr int BM = 256, BN = 128, BK = 64;
-constexpr int LDSTRIDE = BK;        // bytes per LDS row (64: 4 chunks of 16 B, XOR-swizzled)
-constexpr int DEPTH = 4;            // K-steps of global loads in flight
-constexpr int NBUF = 3;             // LDS stages: multiply one, fill one two steps ahead
+constexpr int BM = 256, BN = 128, BK = 128;   // K per iteration; MFMA K is 64
+constexpr int BUF_BYTES = BN * BK;           // one decoded weight tile, 16 KiB
+
+// Slot of a decoded 16-byte group in a buffer: [half h][column block nb][group c][column j],
+// with j XOR-swizzled so that both the writes (4 lanes per row, mixed h and c) and the
+// fragment reads (16 columns of one group) hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int bslot(int h, int nb, int c, int j) {
+    return ((h * 8 + nb) * 64 + c * 16 + (j ^ (4 * (2 * h + (c >> 1))))) * 16;
+}
 
 template <int OUT>
 __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int M, const uint8_t* __restrict__ qp,
     const uint8_t* __restrict__ srel, const float* __restrict__ codebook, const float* __restrict__ ws,
-    const float* __restrict__ bias, int N, int K, int out_type, void* __restrict__ out, int tiles_m, int tiles_n) {
+    const float* __restrict__ bias, int N, int K, void* __restrict__ out, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(16))) uint32_t lut[1024];
-    __shared__ __attribute__((aligned(16))) int8_t As[NBUF][BM * LDSTRIDE];
-    __shared__ __attribute__((aligned(16))) int8_t Bs[NBUF][BN * LDSTRIDE];
-    __shared__ float xs_t[BM], ws_t[BN], bias_t[BN];   // the tile's epilogue scales
+    __shared__ __attribute__((aligned(16))) int8_t Bs[3][BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) float xs_t[BM], ws_t[BN], bias_t[BN];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ntiles = tiles_m * tiles_n;
@@ -56,172 +70,215 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);
     const int tn = pid % tiles_n, tm = pid / tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
+    const int nk = K / BK;   // even, because K % 256 == 0
 
-    build_level_table(lut, codebook, tid, GM_THREADS);
+    // ---- activation operand loads: lane holds row 32*wave + 16*mt + lane%16, 16 bytes
+    // at k = 128*i + 64*h + 16*(lane/16).  Rows past M read row M - 1: they only feed
+    // accumulators whose outputs are never stored.
+    const int8_t* a_ptr[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        const int m = min(m0 + 32 * wave + 16 * mt + (lane & 15), M - 1);
+        a_ptr[mt] = xq + (int64_t)m * K + (lane >> 4) * 16;
+    }
+    struct ASlot {   // one iteration: [h][mt]
+        v4i a00, a01, a10, a11;
+    };
+    auto aload = [&](ASlot& s, int i) __attribute__((always_inline)) {
+        const int k = i * BK;
+        s.a00 = *reinterpret_cast<const v4i*>(a_ptr[0] + k);
+        s.a01 = *reinterpret_cast<const v4i*>(a_ptr[1] + k);
+        s.a10 = *reinterpret_cast<const v4i*>(a_ptr[0] + k + 64);
+        s.a11 = *reinterpret_cast<const v4i*>(a_ptr[1] + k + 64);
+    };
+
+    // ---- weight code loads: thread owns row br = tid / 4 of the tile and the 32 codes
+    // at k = 128*i + 32*(tid%4): half bh = (tid%4)/2, groups bc, bc+1 of that half.
+    const int br = tid >> 2, bq = tid & 3, bh = bq >> 1, bc = 2 * (bq & 1);
+    const int KH = K >> 1, G = K >> 4;
+    const int brow = min(n0 + br, N - 1);
+    const uint8_t* q_ptr = qp + (int64_t)brow * KH + bq * 16;
+    // the 4 scale bytes of half bh are one aligned dword; this thread uses bytes bc, bc+1
+    const uint8_t* s_ptr = srel + (int64_t)brow * G + bh * 4;
+    const int s_shift = 8 * bc;
+    struct CSlot {
+        v4u q;
+        uint32_t s;
+    };
+    auto cload = [&](CSlot& s, int i) __attribute__((always_inline)) {
+        s.q = *reinterpret_cast<const v4u*>(q_ptr + i * (BK / 2));
+        s.s = *reinterpret_cast<const uint32_t*>(s_ptr + i * (BK / 16));
+    };
     const uint4* lut4 = reinterpret_cast<const uint4*>(lut);
-    // epilogue operands of this tile, staged once (rows/columns past the edge get 0)
+    // level-table rows of the two groups (read one half ahead of their decode)
+    auto lut_row = [&](const CSlot& s, int g) __attribute__((always_inline)) {
+        return lut4[(s.s >> (s_shift + 8 * g)) & 0xFFu];
+    };
+    // decode group g of a code slot into buffer buf
+    int w_off[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) w_off[g] = bslot(bh, br >> 4, bc + g, br & 15);
+    auto decode_store = [&](const CSlot& s, const uint4 t, int g, int buf) __attribute__((always_inline)) {
+        const uint2 d0 = decode8(g ? s.q.z : s.q.x, t), d1 = decode8(g ? s.q.w : s.q.y, t);
+        *reinterpret_cast<v4u*>(&Bs[buf][w_off[g]]) = v4u{d0.x, d0.y, d1.x, d1.y};
+    };
+
+    // ---- weight fragment reads: lane holds column 16*nb + lane%16, group lane/16 of half h
+    int r_off[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) r_off[h] = bslot(h, 0, lane >> 4, lane & 15);
+    struct BFrag {
+        v4i b0, b1, b2, b3, b4, b5, b6, b7;
+    };
+    auto bread = [&](BFrag& f, int buf, int h) __attribute__((always_inline)) {
+        const int8_t* p = &Bs[buf][r_off[h]];
+        f.b0 = *reinterpret_cast<const v4i*>(p + 0 * 1024);
+        f.b1 = *reinterpret_cast<const v4i*>(p + 1 * 1024);
+        f.b2 = *reinterpret_cast<const v4i*>(p + 2 * 1024);
+        f.b3 = *reinterpret_cast<const v4i*>(p + 3 * 1024);
+        f.b4 = *reinterpret_cast<const v4i*>(p + 4 * 1024);
+        f.b5 = *reinterpret_cast<const v4i*>(p + 5 * 1024);
+        f.b6 = *reinterpret_cast<const v4i*>(p + 6 * 1024);
+        f.b7 = *reinterpret_cast<const v4i*>(p + 7 * 1024);
+    };
+
+    v4i acc[2][8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    auto mfma_half = [&](const BFrag& f, const v4i& x0, const v4i& x1) __attribute__((always_inline)) {
+        const v4i b[8] = {f.b0, f.b1, f.b2, f.b3, f.b4, f.b5, f.b6, f.b7};
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            acc[0][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b[nb], x0, acc[0][nb], 0, 0, 0);
+            acc[1][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b[nb], x1, acc[1][nb], 0, 0, 0);
+        }
+    };
+
+    // ---- prologue: rings filled, level table and epilogue operands staged, iterations
+    // 0 and 1 decoded, the table rows of iteration 2 and the first-half fragments of
+    // iteration 0 read
+    ASlot A0, A1, A2;
+    CSlot C0, C1, C2;
+    const int last = nk - 1;
+    cload(C0, 0);
+    cload(C1, 1);
+    cload(C2, min(2, last));
+    aload(A0, 0);
+    aload(A1, 1);
+    build_level_table(lut, codebook, tid, GM_THREADS);
     if (tid < BM) xs_t[tid] = m0 + tid < M ? xs[m0 + tid] : 0.0f;
     if (tid < BN) {
         ws_t[tid] = n0 + tid < N ? ws[n0 + tid] : 0.0f;
         bias_t[tid] = (bias && n0 + tid < N) ? bias[n0 + tid] : 0.0f;
     }
-
-    // global -> register roles
-    const int a_row = tid >> 2, a_chk = tid & 3;    // rows a_row and a_row + 128
-    // swizzled position of this thread's chunk (a_chk == b_grp; rows a_row, a_row + 128
-    // and b_row share (row >> 2) & 3)
-    const int w_chunk = (a_chk ^ ((tid >> 4) & 3)) * 16;
-    const int b_row = tid >> 2, b_grp = tid & 3;    // one 16-column group of one weight row
-    const int KH = K >> 1, G = K >> 4;
-    const bool b_ok = n0 + b_row < N;
-    const uint8_t* qp_row = qp + (int64_t)(b_ok ? n0 + b_row : 0) * KH + b_grp * 8;
-    // the 4 scale bytes of a K-step are one aligned dword; this thread uses byte b_grp
-    const uint8_t* sr_row = srel + (int64_t)(b_ok ? n0 + b_row : 0) * G;
-    const int s_shift = 8 * b_grp;
-    // Rows past M (and columns past N) load row 0: they only feed accumulators whose
-    // outputs are never stored, so no masking is needed.
-    const int8_t* a_ptr[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int mr = m0 + a_row + 128 * p;
-        a_ptr[p] = xq + (int64_t)(mr < M ? mr : 0) * K + a_chk * 16;
-    }
-
-    // Register ring of in-flight global loads: slot d holds K-step kt with kt % DEPTH == d.
-    // Step kt+1 is written to LDS while step kt is multiplied, and its slot is refilled
-    // with step kt+1+DEPTH, so every global load has DEPTH steps of MFMA work to land.
-    struct Stage {   // native vector registers only, so the stage lives in VGPRs
-        v4u a0, a1;
-        v2u b;
-        uint32_t s;
-    };
-    // Loads are unconditional (rows past M or N read row 0, steps past the end re-read
-    // the last step) so the count of loads in flight is the same on every path and the
-    // compiler can wait for exactly the oldest stage instead of draining all of them.
-    auto gload = [&](Stage& st, int kt) __attribute__((always_inline)) {
-        const int k0 = kt * BK;
-        st.a0 = *reinterpret_cast<const v4u*>(a_ptr[0] + k0);
-        st.a1 = *reinterpret_cast<const v4u*>(a_ptr[1] + k0);
-        st.b = *reinterpret_cast<const v2u*>(qp_row + (k0 >> 1));
-        st.s = *reinterpret_cast<const uint32_t*>(sr_row + (k0 >> 4));
-    };
-    // Level-table row of a stage's scale byte (one LDS read), then the decode and the
-    // LDS writes of the stage; split so the read can be issued well before its use.
-    auto lut_row = [&](const Stage& st) __attribute__((always_inline)) {
-        return lut4[(st.s >> s_shift) & 0xFFu];
-    };
-    auto lstore = [&](const Stage& st, const uint4 t, int buf) __attribute__((always_inline)) {
-        int8_t* arow = &As[buf][a_row * LDSTRIDE + w_chunk];
-        *reinterpret_cast<v4u*>(arow) = st.a0;
-        *reinterpret_cast<v4u*>(arow + 128 * LDSTRIDE) = st.a1;
-        const uint2 d0 = decode8(st.b.x, t), d1 = decode8(st.b.y, t);
-        *reinterpret_cast<v4u*>(&Bs[buf][b_row * LDSTRIDE + w_chunk]) = v4u{d0.x, d0.y, d1.x, d1.y};
-    };
-
-    const int wm = wave >> 1, wn = wave & 1;   // 4 x 2 waves of 64 x 64
-    v4i acc[4][4];   // [mt][nt] 16 x 16 tiles of the wave's 64 x 64
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-
-    const int nk = K / BK;   // a multiple of DEPTH because K % 256 == 0
-    // v_mfma_i32_16x16x64_i8 operands: lane l holds 16 consecutive k bytes (chunk l / 16 of
-    // the K-step's 64) of row (A) or column (B) l % 16; both operands use the same split.
-    // rows of a fragment are 16-aligned, so the swizzle term (row >> 2) & 3 is (lane >> 2) & 3
-    const int frag_row = lane & 15, frag_k = ((lane >> 4) ^ ((lane >> 2) & 3)) * 16;
-    struct Frags {
-        v4i a0, a1, a2, a3;   // A rows wm*64 + 16*mt + frag_row
-        v4i b0, b1, b2, b3;   // B rows (output columns) wn*64 + 16*nt + frag_row
-    };
-    auto read_frags = [&](Frags& f, int buf) __attribute__((always_inline)) {
-        const int8_t* ab = &As[buf][(wm * 64 + frag_row) * LDSTRIDE + frag_k];
-        const int8_t* bb = &Bs[buf][(wn * 64 + frag_row) * LDSTRIDE + frag_k];
-        f.a0 = *reinterpret_cast<const v4i*>(ab);
-        f.a1 = *reinterpret_cast<const v4i*>(ab + 16 * LDSTRIDE);
-        f.a2 = *reinterpret_cast<const v4i*>(ab + 32 * LDSTRIDE);
-        f.a3 = *reinterpret_cast<const v4i*>(ab + 48 * LDSTRIDE);
-        f.b0 = *reinterpret_cast<const v4i*>(bb);
-        f.b1 = *reinterpret_cast<const v4i*>(bb + 16 * LDSTRIDE);
-        f.b2 = *reinterpret_cast<const v4i*>(bb + 32 * LDSTRIDE);
-        f.b3 = *reinterpret_cast<const v4i*>(bb + 48 * LDSTRIDE);
-    };
-    auto mfma_step = [&](const Frags& f) __attribute__((always_inline)) {
-        const v4i a[4] = {f.a0, f.a1, f.a2, f.a3};
-        const v4i b[4] = {f.b0, f.b1, f.b2, f.b3};
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-                acc[mt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
-    };
-
-    // Pipeline.  Registers: a ring of four K-steps of global loads (named stages: an
-    // indexed private array could be placed in memory by the compiler) and two sets of
-    // MFMA fragments.  LDS: three buffers.  Iteration j: barrier (step j+1 is now in LDS
-    // for everyone); issue the reads of step j+1's fragments; run step j's MFMAs from the
-    // fragments read one iteration earlier, so the LDS reads land while the matrix cores
-    // work; decode step j+2 into the third buffer; refill its ring slot with step
-    // j+2+DEPTH.
-    Stage r0, r1, r2, r3;
-    gload(r0, 0);
-    gload(r1, min(1, nk - 1));
-    gload(r2, min(2, nk - 1));
-    gload(r3, min(3, nk - 1));
-    __syncthreads();   // level table ready
-    lstore(r0, lut_row(r0), 0);
-    lstore(r1, lut_row(r1), 1);
-    gload(r0, min(4, nk - 1));
-    gload(r1, min(5, nk - 1));
     __syncthreads();
-    Frags f0, f1;
-    read_frags(f0, 0);
+    decode_store(C0, lut_row(C0, 0), 0, 0);
+    decode_store(C0, lut_row(C0, 1), 1, 0);
+    decode_store(C1, lut_row(C1, 0), 0, 1);
+    decode_store(C1, lut_row(C1, 1), 1, 1);
+    cload(C0, min(3, last));
+    cload(C1, min(4, last));
+    uint4 T0 = lut_row(C2, 0), T1 = lut_row(C2, 1);
+    __syncthreads();
+    BFrag F0, F1;
+    bread(F0, 0, 0);
 
-    auto step = [&](int j, const Frags& cur, Frags& nxt, Stage& st) __attribute__((always_inline)) {
+    // Iteration i, with a = activations of i, a_next = the slot to refill with i + 2,
+    // c = codes of i + 2 (their table rows T0, T1 already read), c_next = codes of i + 3:
+    //   first half : read the second-half fragments of i (buffer rd), refill a_next,
+    //                16 MFMAs on the first half interleaved with the decode of group 0
+    //                of c into buffer wr, then read c_next's first table row
+    //   second half: read the first-half fragments of i + 1 (buffer rd_next), 16 MFMAs
+    //                on the second half interleaved with the decode of group 1 of c,
+    //                then read c_next's second table row and refill c with i + 5
+    //   barrier    : buffer wr is complete for everyone, and buffer rd is free to be
+    //                overwritten by the next iteration
+    // Past the end, loads re-read the last iteration and decodes write a buffer nobody
+    // reads, so the loop body has no branches.
+    auto iter = [&](int i, const int rd, const int rd_next, const int wr, ASlot& a, ASlot& a_next, CSlot& c,
+                    CSlot& c_next) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        bread(F1, rd, 1);
+        aload(a_next, min(i + 2, last));
+        mfma_half(F0, a.a00, a.a01);
+        decode_store(c, T0, 0, wr);
+        T0 = lut_row(c_next, 0);
+        // issue order: each MFMA followed by a share of the fragment reads, loads and
+        // decode, so the memory pipelines see a steady stream instead of bursts
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+            if (k % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // fragment read
+            if (k % 4 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // activation load
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);                  // decode
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // decoded group
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next table row
+        __builtin_amdgcn_sched_barrier(0);
+        bread(F0, rd_next, 0);
+        mfma_half(F1, a.a10, a.a11);
+        decode_store(c, T1, 1, wr);
+        T1 = lut_row(c_next, 1);
+        cload(c, min(i + 5, last));
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (k % 2 == 0 && k < 14) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (k == 14) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            if (k == 9) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            if (k == 11 || k == 13) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        const uint4 t = lut_row(st);
-        read_frags(nxt, (j + 1) % NBUF);   // past the end: reads a buffer nobody uses
-        mfma_step(cur);
-        lstore(st, t, (j + 2) % NBUF);     // past the end: a harmless write to a buffer nobody reads
-        gload(st, min(j + 2 + DEPTH, nk - 1));
-        // issue order: the table read, the 8 fragment reads, then the 16 MFMAs each
-        // followed by a few decode instructions, then the LDS writes and global loads
-        __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x200, 3, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
-        __builtin_amdgcn_sched_barrier(0);
     };
-    for (int kt0 = 0; kt0 < nk; kt0 += DEPTH) {
-        step(kt0 + 0, f0, f1, r2);
-        step(kt0 + 1, f1, f0, r3);
-        step(kt0 + 2, f0, f1, r0);
-        step(kt0 + 3, f1, f0, r1);
+    int i = 0;
+    for (; i + 3 <= nk; i += 3) {
+        iter(i + 0, 0, 1, 2, A0, A2, C2, C0);
+        iter(i + 1, 1, 2, 0, A1, A0, C0, C1);
+        iter(i + 2, 2, 0, 1, A2, A1, C1, C2);
     }
+    if (i < nk) iter(i + 0, 0, 1, 2, A0, A2, C2, C0);
+    if (i + 1 < nk) iter(i + 1, 1, 2, 0, A1, A0, C0, C1);
 
-    // epilogue: register r of a 16 x 16 accumulator tile holds row 4*(lane/16) + r, column
-    // lane % 16; stores of rows past M / columns past N are skipped
-    const bool interior = m0 + BM <= M && n0 + BN <= N;
+    // ---- epilogue: accumulator (mt, nb) register r of lane l holds column
+    // 16*nb + 4*(l/16) + r of row 32*wave + 16*mt + l%16
+    const bool vec = m0 + BM <= M && n0 + BN <= N && (N & 3) == 0;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int nl = wn * 64 + nt * 16 + (lane & 15), n = n0 + nl;
-        const float wsn = ws_t[nl], bn = bias_t[nl];
-        const bool n_ok = n < N;
+    for (int mt = 0; mt < 2; ++mt) {
+        const int ml = 32 * wave + 16 * mt + (lane & 15), m = m0 + ml;
+        const float xsm = xs_t[ml];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int nb = 0; nb < 8; ++nb) {
+            const int nl = 16 * nb + 4 * (lane >> 4), n = n0 + nl;
+            const float4 wv = *reinterpret_cast<const float4*>(&ws_t[nl]);
+            const float4 bv = *reinterpret_cast<const float4*>(&bias_t[nl]);
+            const v4i a = acc[mt][nb];
+            float y[4];
+            const float wsv[4] = {wv.x, wv.y, wv.z, wv.w}, bsv[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int ml = wm * 64 + mt * 16 + 4 * (lane >> 4) + r, m = m0 + ml;
-                const int32_t a = acc[mt][nt][r];
-                float y = __fmul_rn((float)a, __fmul_rn(xs_t[ml], wsn));
-                if (bias) y = __fadd_rn(y, bn);
-                if (interior || (n_ok && m < M)) store_out(out, OUT, (int64_t)m * N + n, a, y);
+                y[r] = __fmul_rn((float)a[r], __fmul_rn(xsm, wsv[r]));
+                if (bias) y[r] = __fadd_rn(y[r], bsv[r]);
+            }
+            const int64_t idx = (int64_t)m * N + n;
+            if (vec) {
+                if (OUT == 0) {
+                    uint2 p;
+                    p.x = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
+                    p.y = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
+                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + idx) = p;
+                } else if (OUT == 1) {
+                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + idx) = float4{y[0], y[1], y[2], y[3]};
+                } else {
+                    *reinterpret_cast<v4i*>(reinterpret_cast<int32_t*>(out) + idx) = a;
+                }
+            } else if (m < M) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < N) store_out(out, OUT, idx + r, a[r], y[r]);
             }
         }
     }
@@ -237,14 +294,14 @@ hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, const uint8_t* 
     const int64_t ntiles = (int64_t)tiles_m * tiles_n;
     const dim3 g((unsigned)ntiles), b(GM_THREADS);
     if (out_type == 0)
-        hipLaunchKernelGGL(gemm_kernel<0>, g, b, 0, stream, xq, xs, M, qp, srel, codebook, ws, bias, N, K, out_type,
-                           out, tiles_m, tiles_n);
+        hipLaunchKernelGGL(gemm_kernel<0>, g, b, 0, stream, xq, xs, M, qp, srel, codebook, ws, bias, N, K, out,
+                           tiles_m, tiles_n);
     else if (out_type == 1)
-        hipLaunchKernelGGL(gemm_kernel<1>, g, b, 0, stream, xq, xs, M, qp, srel, codebook, ws, bias, N, K, out_type,
-                           out, tiles_m, tiles_n);
+        hipLaunchKernelGGL(gemm_kernel<1>, g, b, 0, stream, xq, xs, M, qp, srel, codebook, ws, bias, N, K, out,
+                           tiles_m, tiles_n);
     else
-        hipLaunchKernelGGL(gemm_kernel<2>, g, b, 0, stream, xq, xs, M, qp, srel, codebook, ws, bias, N, K, out_type,
-                           out, tiles_m, tiles_n);
+        hipLaunchKernelGGL(gemm_kernel<2>, g, b, 0, stream, xq, xs, M, qp, srel, codebook, ws, bias, N, K, out,
+                           tiles_m, tiles_n);
     return hipGetLastError();
 }
 
