@@ -19,6 +19,8 @@ hipError_t launch_gemv(const int8_t* xq, const float* xs, int M, const uint8_t* 
 hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, const uint8_t* qp, const uint8_t* srel,
                        const float* codebook, const float* ws, const float* bias, int N, int K, int out_type,
                        void* out, hipStream_t stream);
+hipError_t launch_quantize(const float* w, int64_t N, int K, int rotated, const float* codebook, uint8_t* qpacked,
+                           uint8_t* srel, float* s_channel, hipStream_t stream);
 }  // namespace w4a8
 
 namespace {
@@ -114,6 +116,20 @@ int w4a8_gemv(const int8_t* xq, const float* xs, int64_t M, const uint8_t* qpack
                                       out_type, out, static_cast<hipStream_t>(stream)));
 }
 
+int quantize_w4(const float* w, int64_t N, int64_t K, int32_t rot_block, int32_t group, int32_t rotated,
+                const float* codebook, uint8_t* qpacked, uint8_t* srel, float* s_channel, void* stream) {
+    int st = check_n(N);
+    if (st) return st;
+    if ((st = check_k(K))) return st;
+    if (rot_block != W4A8_ROT_BLOCK || group != W4A8_GROUP) return W4A8_ERR_UNSUPPORTED;
+    if (!w || !codebook || !qpacked || !srel || !s_channel) return W4A8_ERR_INVALID_ARG;
+    if (!aligned(w, 16) || !aligned(codebook, 4) || !aligned(qpacked, 16) || !aligned(srel, 16) ||
+        !aligned(s_channel, 4))
+        return W4A8_ERR_ALIGN;
+    return launched(w4a8::launch_quantize(w, N, (int)K, rotated, codebook, qpacked, srel, s_channel,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 const char* w4a8_status_string(int status) {
     switch (status) {
         case W4A8_OK: return "W4A8_OK";
@@ -126,6 +142,6 @@ const char* w4a8_status_string(int status) {
     }
 }
 
-int w4a8_abi_version(void) { return 1; }
+int w4a8_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -37,6 +37,16 @@ def gaussian_weight(n: int, k: int, seed: int, std: float = 0.02) -> np.ndarray:
     return (rng(seed).standard_normal((n, k)) * std).astype(np.float32)
 
 
+def gaussian_weight_device(n: int, k: int, seed: int, device, std: float = 0.02):
+    """fp32 torch tensor [n, k] of i.i.d. N(0, std^2) entries drawn on ``device`` by
+    torch's generator seeded with ``seed`` (a different stream from gaussian_weight;
+    for large benchmark weight sets that would be slow to draw on the host)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(n, k, generator=g, device=device, dtype=torch.float32) * std
+
+
 def activations(m: int, k: int, seed: int, kind: str = "normal", nu: float = 4.0,
                 outlier_frac: float = 0.01, outlier_scale: float = 20.0,
                 outlier_seed: int | None = None) -> np.ndarray:

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so"
 OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP = range(6)
 OUT_BF16, OUT_F32, OUT_I32 = 0, 1, 2
 ROT_BLOCK, GROUP, GEMV_MAX_M, MAX_K = 256, 16, 8, 131072
+ABI_VERSION = 2
 _OUT_CODES = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32, torch.int32: OUT_I32}
 
 # The default 16-level table (ai-toolkit convrot_w4a8_quant.py, FIXED_CODEBOOK):
@@ -41,6 +42,7 @@ SIGNATURES = {
     "decode_w4_to_int8": [_P, _P, _P, _I64, _I64, _I32, _P, _P],
     "w4a8_gemm": [_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P],
     "w4a8_gemv": [_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P],
+    "quantize_w4": [_P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P],
     "w4a8_status_string": [ctypes.c_int],
     "w4a8_abi_version": [],
 }
@@ -70,7 +72,7 @@ def load() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_char_p if name == "w4a8_status_string" else ctypes.c_int
-        if lib.w4a8_abi_version() != 1:
+        if lib.w4a8_abi_version() != ABI_VERSION:
             raise ImportError("libw4a8.so ABI version mismatch")
         _lib = lib
     return _lib
@@ -204,6 +206,24 @@ def w4a8_gemm(xq, xs, layer: W4A8Layer, out_dtype=torch.bfloat16, out=None):
 
 def w4a8_gemv(xq, xs, layer: W4A8Layer, out_dtype=torch.bfloat16, out=None):
     return _linear_call("w4a8_gemv", xq, xs, layer, out_dtype, out)
+
+
+def quantize_w4(w: torch.Tensor, codebook=None, rotated: bool = False, bias=None) -> W4A8Layer:
+    """fp32 weight [N, K] on the GPU -> W4A8Layer (packed codes, fp8 group scales,
+    channel scales).  ``rotated`` says the weight is already in the rotated basis.
+    ``codebook`` defaults to FIXED_CODEBOOK and must be sorted ascending."""
+    _dev(w, torch.float32, "w")
+    n, k = w.shape
+    cb = torch.tensor(FIXED_CODEBOOK if codebook is None else codebook, dtype=torch.float32, device=w.device) \
+        if not isinstance(codebook, torch.Tensor) else _dev(codebook, torch.float32, "codebook")
+    qp = torch.empty(n, k // 2, dtype=torch.uint8, device=w.device)
+    sr = torch.empty(n, k // GROUP, dtype=torch.uint8, device=w.device)
+    sch = torch.empty(n, dtype=torch.float32, device=w.device)
+    _check("quantize_w4", load().quantize_w4(w.data_ptr(), n, k, ROT_BLOCK, GROUP, int(bool(rotated)), cb.data_ptr(),
+                                             qp.data_ptr(), sr.data_ptr(), sch.data_ptr(), _stream(w)))
+    if bias is not None:
+        bias = _dev(bias, torch.float32, "bias")
+    return W4A8Layer(qp, sr, cb, sch, bias)
 
 
 def linear(x: torch.Tensor, layer: W4A8Layer, out_dtype=torch.bfloat16) -> torch.Tensor:

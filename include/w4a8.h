@@ -31,7 +31,7 @@
  *     returns an error has enqueued nothing and written nothing.
  *   - Return value: W4A8_OK (0) or one of the W4A8_ERR_* codes below.  No exception
  *     crosses the ABI.  w4a8_status_string() names a code.
- *   - Alignment: x, xq, qpacked, srel, w8 and out must be 16-byte aligned; xs,
+ *   - Alignment: x, w, xq, qpacked, srel, w8 and out must be 16-byte aligned; xs,
  *     codebook, s_channel and bias 4-byte aligned.
  *   - Sizes: M >= 0 (M == 0 is a valid call that does nothing), N >= 1,
  *     256 <= K <= W4A8_MAX_K with K % 256 == 0 (the bound keeps every int32
@@ -131,6 +131,34 @@ int w4a8_gemv(const int8_t* xq, const float* xs, int64_t M,
               const uint8_t* qpacked, const uint8_t* srel, const float* codebook,
               const float* s_channel, const float* bias, int64_t N, int64_t K, int32_t group,
               int32_t out_type, void* out, void* stream);
+
+/*
+ * quantize_w4 -- the weight quantiser: an fp32 weight to the layer storage above.
+ *
+ * ai-toolkit ConvRotW4A8Quantizer.quantize_ (the weight is first rotated like the
+ * activations, h3-rs fn hadamard with block 256, exact product rounded once to fp32)
+ * and _quantize_rotated_rows with _assign_codes, grid_levels and _assign_grid:
+ * per group of 16 the absmax scale, the nearest codebook level, two least-squares
+ * refinements of the group scale (sums of fp32 products accumulated in column order,
+ * rounded once to fp32), the channel scale max |level * scale| / 127, the fp8 e4m3
+ * relative group scale (round to nearest even, above 464 -> NaN byte), and the final
+ * codes as the nearest int8-grid levels of w / s_channel.  Nearest means: among the
+ * two levels around the value (by the count of levels below it), the upper one only
+ * if it is strictly closer.  Rows are independent; the result is deterministic.
+ *
+ *   w          in   float [N, K]: the weight, or the already rotated weight if rotated != 0
+ *   N, K            sizes (limits as above)
+ *   rot_block       must be 256
+ *   group           must be 16
+ *   rotated         0: rotate w first; nonzero: w is already in the rotated basis
+ *   codebook   in   float [16], sorted ascending
+ *   qpacked    out  uint8 [N, K/2]
+ *   srel       out  uint8 [N, K/16]
+ *   s_channel  out  float [N]
+ * Weights must be finite.  Alignment: w 16 bytes.
+ */
+int quantize_w4(const float* w, int64_t N, int64_t K, int32_t rot_block, int32_t group, int32_t rotated,
+                const float* codebook, uint8_t* qpacked, uint8_t* srel, float* s_channel, void* stream);
 
 /* Name of a status code ("W4A8_OK", ...); never NULL. */
 const char* w4a8_status_string(int status);

@@ -25,12 +25,12 @@ def w4a8():
     return b
 
 
-def test_header_declares_the_four_operations():
+def test_header_declares_the_operations():
     names = _declared_functions()
-    for n in ("rotate_quant_act", "decode_w4_to_int8", "w4a8_gemm", "w4a8_gemv", "w4a8_status_string",
-              "w4a8_abi_version"):
+    for n in ("rotate_quant_act", "decode_w4_to_int8", "w4a8_gemm", "w4a8_gemv", "quantize_w4",
+              "w4a8_status_string", "w4a8_abi_version"):
         assert n in names
-    assert len(names) == 6, names
+    assert len(names) == 7, names
 
 
 def test_library_exports_every_declared_symbol(w4a8):
@@ -45,7 +45,7 @@ def test_status_strings(w4a8):
         "W4A8_OK", "W4A8_ERR_INVALID_ARG", "W4A8_ERR_SHAPE", "W4A8_ERR_ALIGN", "W4A8_ERR_UNSUPPORTED",
         "W4A8_ERR_HIP"]
     assert w4a8.status_string(99) == "W4A8_ERR_UNKNOWN"
-    assert w4a8.load().w4a8_abi_version() == 1
+    assert w4a8.load().w4a8_abi_version() == w4a8.ABI_VERSION == 2
 
 
 A = 1 << 20          # a 16-byte-aligned fake address (never dereferenced: validation fails first)
@@ -108,10 +108,25 @@ def test_decode_validation(w4a8):
     assert c(w8=A + 4) == w4a8.ERR_ALIGN and c(srel=A + 8) == w4a8.ERR_ALIGN
 
 
+def test_quantize_validation(w4a8):
+    c = lambda **kw: w4a8.call("quantize_w4", kw.get("w", A), kw.get("N", 8), kw.get("K", 256), kw.get("rot", 256),
+                               kw.get("group", 16), kw.get("rotated", 0), kw.get("cb", A), kw.get("qp", A),
+                               kw.get("srel", A), kw.get("sch", A), None)
+    assert c(N=0) == w4a8.ERR_SHAPE and c(N=-1) == w4a8.ERR_INVALID_ARG
+    assert c(K=272) == w4a8.ERR_SHAPE and c(K=-256) == w4a8.ERR_INVALID_ARG
+    assert c(rot=64) == w4a8.ERR_UNSUPPORTED and c(group=32) == w4a8.ERR_UNSUPPORTED
+    for p in ("w", "cb", "qp", "srel", "sch"):
+        assert c(**{p: None}) == w4a8.ERR_INVALID_ARG, p
+    assert c(w=A + 4) == w4a8.ERR_ALIGN and c(qp=A + 8) == w4a8.ERR_ALIGN and c(srel=A + 1) == w4a8.ERR_ALIGN
+    assert c(cb=A + 2) == w4a8.ERR_ALIGN and c(sch=A + 2) == w4a8.ERR_ALIGN
+
+
 def test_binding_rejects_cpu_tensors(w4a8):
     import torch
     with pytest.raises(ValueError):
         w4a8.rotate_quant_act(torch.zeros(2, 256, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        w4a8.quantize_w4(torch.zeros(2, 256, dtype=torch.float32))
 
 
 def test_binding_default_codebook_matches_the_page_table():
