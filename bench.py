@@ -177,6 +177,52 @@ def bench_gemv(args, torch, B, device):
     return res
 
 
+def bench_decode_set(args, torch, B, device):
+    """The 64-layer decode set at M=1 (16 layers each of 3072x3072, 9216x3072,
+    12288x3072, 3072x12288; 1.02 GB of weights, four times the Infinity Cache): one
+    w4a8_gemv launch per layer, and one w4a8_gemv_grouped call (32 layers per launch)
+    for layers that are independent of each other.  GPU time of the whole set."""
+    from bit_codebook_quantized_amd import synth
+    shapes = [(3072, 3072), (9216, 3072), (12288, 3072), (3072, 12288)]
+    items, wbytes = [], 0
+    for i in range(64):
+        n, k = shapes[i // 16]
+        w = synth.gaussian_weight_device(n, k, seed=synth.seed_for(4, i, synth.ROLE_WEIGHT), device=device)
+        layer = B.quantize_w4(w)
+        del w
+        x = torch.from_numpy(synth.activations(1, k, seed=synth.seed_for(4, i, synth.ROLE_ACT))).to(
+            torch.bfloat16).to(device)
+        xq, xs = B.rotate_quant_act(x)
+        out = torch.empty(1, n, dtype=torch.bfloat16, device=device)
+        items.append((xq, xs, layer, out))
+        wbytes += weight_bytes(n, k)
+    single = [B.prepared_linear("w4a8_gemv", xq, xs, layer, out) for xq, xs, layer, out in items]
+    grouped = B.prepared_gemv_grouped(items)
+
+    def timed_set(calls, reps):
+        pairs = event_pairs(torch, reps)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(args.sleep_cycles))
+        for r in range(reps):
+            pairs[r][0].record()
+            for c in calls:
+                c()
+            pairs[r][1].record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in pairs]))
+
+    timed_set(single, 2)
+    timed_set([grouped], 2)
+    seq_ms = timed_set(single, 10)
+    grp_ms = timed_set([grouped], 10)
+    return {"layers": 64, "M": 1, "weight_bytes": wbytes,
+            "per_layer_launches_us": round(seq_ms * 1e3, 1),
+            "per_layer_weight_GBps": round(wbytes / (seq_ms * 1e-3) / 1e9, 1),
+            "grouped_us": round(grp_ms * 1e3, 1),
+            "grouped_weight_GBps": round(wbytes / (grp_ms * 1e-3) / 1e9, 1),
+            "grouped_frac": round(wbytes / (grp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 def cpu_baseline(pre, min_seconds=10.0):
     """The oracle, untuned, on the host cores: the whole M=2048 layer step (rotate +
     quantise, decode, exact contraction, epilogue), repeated until at least
@@ -254,6 +300,7 @@ def main():
 
     pre = bench_prefill(args, torch, B, device)
     gemv = None if args.no_gemv else bench_gemv(args, torch, B, device)
+    decode_set = None if args.no_gemv else bench_decode_set(args, torch, B, device)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre)
 
     tops = pre["ops"] / pre["wall_s"] / 1e12
@@ -285,6 +332,7 @@ def main():
                              "GBps": round(pre["rq_bytes"] / (pre["rq_ms"] * 1e-3) / 1e9, 1),
                              "frac_hbm": round(pre["rq_bytes"] / (pre["rq_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "gemv": gemv,
+        "gemv_decode_set": decode_set,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

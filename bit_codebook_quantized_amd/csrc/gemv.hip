@@ -24,6 +24,7 @@
 // registers for the whole of K and are combined across the wave once, by a
 // reduce-scatter (each halving step exchanges half the values), so a lane ends
 // with one fully summed output.
+#include "../../include/w4a8.h"
 #include "w4a8_device.hpp"
 
 namespace w4a8 {
@@ -31,6 +32,7 @@ namespace {
 
 constexpr int GV_THREADS = 256;
 constexpr int GV_BATCH = 4;   // groups per lane per batch
+constexpr int GEMV_GROUP_MAX = 32;   // layers per grouped launch (the table fits the kernel arguments)
 
 constexpr int pow2_ceil(int v) { return v <= 1 ? 1 : 2 * pow2_ceil((v + 1) / 2); }
 constexpr int log2i(int v) { return v <= 1 ? 0 : 1 + log2i(v / 2); }
@@ -72,13 +74,11 @@ __device__ __forceinline__ void stage_acts(uint8_t* act, const int8_t* __restric
 }
 
 template <int MM, int R>
-__global__ __launch_bounds__(GV_THREADS) void gemv_kernel(const int8_t* __restrict__ xq, const float* __restrict__ xs,
-                                                          const uint8_t* __restrict__ qp,
-                                                          const uint8_t* __restrict__ srel,
-                                                          const float* __restrict__ codebook,
-                                                          const float* __restrict__ ws,
-                                                          const float* __restrict__ bias, int N, int K,
-                                                          int out_type, void* __restrict__ out) {
+__device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const float* __restrict__ xs,
+                                          const uint8_t* __restrict__ qp, const uint8_t* __restrict__ srel,
+                                          const float* __restrict__ codebook, const float* __restrict__ ws,
+                                          const float* __restrict__ bias, int N, int K, int out_type,
+                                          void* __restrict__ out, int block) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint32_t* lut = reinterpret_cast<uint32_t*>(smem);
     uint8_t* act = smem + 4096;
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(const int8_t* __restri
     constexpr int SLAB = slab_cols(MM);
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n0 = (blockIdx.x * (GV_THREADS / 64) + wave) * R;
+    const int n0 = (block * (GV_THREADS / 64) + wave) * R;
     const int KH = K >> 1, G = K >> 4, nchunk = K >> 4;
 
     const uint8_t* qrow[R];
@@ -180,14 +180,76 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(const int8_t* __restri
     }
 }
 
+template <int MM, int R>
+__global__ __launch_bounds__(GV_THREADS) void gemv_kernel(const int8_t* __restrict__ xq, const float* __restrict__ xs,
+                                                          const uint8_t* __restrict__ qp,
+                                                          const uint8_t* __restrict__ srel,
+                                                          const float* __restrict__ codebook,
+                                                          const float* __restrict__ ws,
+                                                          const float* __restrict__ bias, int N, int K,
+                                                          int out_type, void* __restrict__ out) {
+    gemv_body<MM, R>(xq, xs, qp, srel, codebook, ws, bias, N, K, out_type, out, blockIdx.x);
+}
+
+// Several independent layers (same M) in one launch: block b works on the layer whose
+// range [first[l], first[l+1]) of block ids holds b, as block b - first[l] of it.  The
+// layer table travels in the kernel arguments.
+struct GroupArgs {
+    int count;
+    int first[GEMV_GROUP_MAX + 1];
+    w4a8_gemv_layer layer[GEMV_GROUP_MAX];
+};
+
+template <int MM, int R>
+__global__ __launch_bounds__(GV_THREADS) void gemv_grouped_kernel(const GroupArgs args, int out_type) {
+    int l = 0;
+    while (l + 1 < args.count && (int)blockIdx.x >= args.first[l + 1]) ++l;   // uniform: a few steps
+    const w4a8_gemv_layer& L = args.layer[l];
+    gemv_body<MM, R>(L.xq, L.xs, L.qpacked, L.srel, L.codebook, L.s_channel, L.bias, (int)L.N, (int)L.K,
+                     out_type, L.out, blockIdx.x - args.first[l]);
+}
+
+// rows per wave: as many as keep >= 2048 waves in the grid (8 per compute unit), at most 4
+int rows_per_wave(int64_t rows) {
+    int R = 4;
+    while (R > 1 && (rows + R - 1) / R < 2048) R >>= 1;
+    return R;
+}
+
+template <int MM>
+hipError_t launch_gemv_grouped_m(const w4a8_gemv_layer* layers, int count, int out_type, hipStream_t stream) {
+    int64_t rows = 0;
+    for (int i = 0; i < count; ++i) rows += layers[i].N;
+    const int R = rows_per_wave(rows), per_block = (GV_THREADS / 64) * R;
+    for (int base = 0; base < count; base += GEMV_GROUP_MAX) {
+        GroupArgs a;
+        a.count = count - base < GEMV_GROUP_MAX ? count - base : GEMV_GROUP_MAX;
+        a.first[0] = 0;
+        for (int i = 0; i < a.count; ++i) {
+            a.layer[i] = layers[base + i];
+            a.first[i + 1] = a.first[i] + (int)((layers[base + i].N + per_block - 1) / per_block);
+        }
+        for (int i = a.count; i < GEMV_GROUP_MAX; ++i) a.first[i + 1] = a.first[a.count];
+        const size_t lds = 4096 + (size_t)MM * slab_cols(MM);
+        const dim3 g(a.first[a.count]), b(GV_THREADS);
+        if (R == 4)
+            hipLaunchKernelGGL((gemv_grouped_kernel<MM, 4>), g, b, lds, stream, a, out_type);
+        else if (R == 2)
+            hipLaunchKernelGGL((gemv_grouped_kernel<MM, 2>), g, b, lds, stream, a, out_type);
+        else
+            hipLaunchKernelGGL((gemv_grouped_kernel<MM, 1>), g, b, lds, stream, a, out_type);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 template <int MM>
 hipError_t launch_gemv_m(const int8_t* xq, const float* xs, const uint8_t* qp, const uint8_t* srel,
                          const float* codebook, const float* ws, const float* bias, int N, int K, int out_type,
                          void* out, hipStream_t stream) {
-    // rows per wave: as many as keep >= 2048 waves in the grid (8 per compute unit), at most 4
     const int waves_per_block = GV_THREADS / 64;
-    int R = 4;
-    while (R > 1 && (N + R - 1) / R < 2048) R >>= 1;
+    const int R = rows_per_wave(N);
     const int blocks = (N + waves_per_block * R - 1) / (waves_per_block * R);
     const size_t lds = 4096 + (size_t)MM * slab_cols(MM);
     const dim3 g(blocks), b(GV_THREADS);
@@ -204,6 +266,21 @@ hipError_t launch_gemv_m(const int8_t* xq, const float* xs, const uint8_t* qp, c
 }
 
 }  // namespace
+
+hipError_t launch_gemv_grouped(const w4a8_gemv_layer* layers, int count, int M, int out_type, hipStream_t stream) {
+    (void)hipGetLastError();   // clear a stale error so the checks below are about these launches
+    switch (M) {
+        case 1: return launch_gemv_grouped_m<1>(layers, count, out_type, stream);
+        case 2: return launch_gemv_grouped_m<2>(layers, count, out_type, stream);
+        case 3: return launch_gemv_grouped_m<3>(layers, count, out_type, stream);
+        case 4: return launch_gemv_grouped_m<4>(layers, count, out_type, stream);
+        case 5: return launch_gemv_grouped_m<5>(layers, count, out_type, stream);
+        case 6: return launch_gemv_grouped_m<6>(layers, count, out_type, stream);
+        case 7: return launch_gemv_grouped_m<7>(layers, count, out_type, stream);
+        case 8: return launch_gemv_grouped_m<8>(layers, count, out_type, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_gemv(const int8_t* xq, const float* xs, int M, const uint8_t* qp, const uint8_t* srel,
                        const float* codebook, const float* ws, const float* bias, int N, int K, int out_type,

@@ -19,6 +19,7 @@ hipError_t launch_gemv(const int8_t* xq, const float* xs, int M, const uint8_t* 
 hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, const uint8_t* qp, const uint8_t* srel,
                        const float* codebook, const float* ws, const float* bias, int N, int K, int out_type,
                        void* out, hipStream_t stream);
+hipError_t launch_gemv_grouped(const w4a8_gemv_layer* layers, int count, int M, int out_type, hipStream_t stream);
 hipError_t launch_quantize(const float* w, int64_t N, int K, int rotated, const float* codebook, uint8_t* qpacked,
                            uint8_t* srel, float* s_channel, hipStream_t stream);
 }  // namespace w4a8
@@ -116,6 +117,24 @@ int w4a8_gemv(const int8_t* xq, const float* xs, int64_t M, const uint8_t* qpack
                                       out_type, out, static_cast<hipStream_t>(stream)));
 }
 
+int w4a8_gemv_grouped(const w4a8_gemv_layer* layers, int32_t count, int64_t M, int32_t group, int32_t out_type,
+                      void* stream) {
+    if (count < 0 || M < 0) return W4A8_ERR_INVALID_ARG;
+    if (M > W4A8_GEMV_MAX_M) return W4A8_ERR_UNSUPPORTED;
+    if (count > 0 && !layers) return W4A8_ERR_INVALID_ARG;
+    int64_t rows = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const w4a8_gemv_layer& L = layers[i];
+        const int st = check_linear(L.xq, L.xs, M, L.qpacked, L.srel, L.codebook, L.s_channel, L.bias, L.N, L.K,
+                                    group, out_type, L.out);
+        if (st) return st;
+        rows += L.N;
+        if (rows > MAX_ROWS) return W4A8_ERR_SHAPE;
+    }
+    if (count == 0 || M == 0) return W4A8_OK;
+    return launched(w4a8::launch_gemv_grouped(layers, count, (int)M, out_type, static_cast<hipStream_t>(stream)));
+}
+
 int quantize_w4(const float* w, int64_t N, int64_t K, int32_t rot_block, int32_t group, int32_t rotated,
                 const float* codebook, uint8_t* qpacked, uint8_t* srel, float* s_channel, void* stream) {
     int st = check_n(N);
@@ -142,6 +161,6 @@ const char* w4a8_status_string(int status) {
     }
 }
 
-int w4a8_abi_version(void) { return 2; }
+int w4a8_abi_version(void) { return 3; }
 
 }  // extern "C"

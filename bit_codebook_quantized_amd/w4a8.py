@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so"
 OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP = range(6)
 OUT_BF16, OUT_F32, OUT_I32 = 0, 1, 2
 ROT_BLOCK, GROUP, GEMV_MAX_M, MAX_K = 256, 16, 8, 131072
-ABI_VERSION = 2
+ABI_VERSION = 3
 _OUT_CODES = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32, torch.int32: OUT_I32}
 
 # The default 16-level table (ai-toolkit convrot_w4a8_quant.py, FIXED_CODEBOOK):
@@ -43,11 +43,18 @@ SIGNATURES = {
     "w4a8_gemm": [_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P],
     "w4a8_gemv": [_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P],
     "quantize_w4": [_P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P],
+    "w4a8_gemv_grouped": [_P, _I32, _I64, _I32, _I32, _P],
     "w4a8_status_string": [ctypes.c_int],
     "w4a8_abi_version": [],
 }
 
 _lib = None
+
+
+class GemvLayerDesc(ctypes.Structure):
+    """Mirror of struct w4a8_gemv_layer in include/w4a8.h."""
+    _fields_ = [("xq", _P), ("xs", _P), ("qpacked", _P), ("srel", _P), ("codebook", _P), ("s_channel", _P),
+                ("bias", _P), ("out", _P), ("N", _I64), ("K", _I64)]
 
 
 class W4A8Error(RuntimeError):
@@ -206,6 +213,56 @@ def w4a8_gemm(xq, xs, layer: W4A8Layer, out_dtype=torch.bfloat16, out=None):
 
 def w4a8_gemv(xq, xs, layer: W4A8Layer, out_dtype=torch.bfloat16, out=None):
     return _linear_call("w4a8_gemv", xq, xs, layer, out_dtype, out)
+
+
+def _group_descs(items, out_dtype):
+    """items: (xq, xs, layer, out or None) per layer, common M -> (ctypes array, outs, M)."""
+    if out_dtype not in _OUT_CODES:
+        raise ValueError(f"unsupported out_dtype {out_dtype}")
+    arr = (GemvLayerDesc * max(len(items), 1))()
+    outs, m = [], None
+    for i, (xq, xs, layer, out) in enumerate(items):
+        layer.check()
+        _dev(xq, torch.int8, "xq")
+        _dev(xs, torch.float32, "xs")
+        mi, k = xq.shape
+        if m is None:
+            m = mi
+        if mi != m or tuple(xs.shape) != (m,) or k != layer.in_features:
+            raise ValueError(f"layer {i}: activations do not match (M must be common to all layers)")
+        n = layer.out_features
+        out = _out(out, (m, n), out_dtype, xq.device, "out")
+        outs.append(out)
+        arr[i] = GemvLayerDesc(xq.data_ptr(), xs.data_ptr(), layer.qpacked.data_ptr(), layer.srel.data_ptr(),
+                               layer.codebook.data_ptr(), layer.s_channel.data_ptr(),
+                               layer.bias.data_ptr() if layer.bias is not None else None, out.data_ptr(), n, k)
+    return arr, outs, (m or 0)
+
+
+def w4a8_gemv_grouped(items, out_dtype=torch.bfloat16):
+    """The GEMV of several independent layers, 32 per launch.  items: list of
+    (xq [M, K], xs [M], W4A8Layer, out [M, N] or None) with a common M <= 8.
+    Returns the outputs (bit-identical to w4a8_gemv on each layer)."""
+    arr, outs, m = _group_descs(items, out_dtype)
+    if items:
+        _check("w4a8_gemv_grouped", load().w4a8_gemv_grouped(ctypes.addressof(arr), len(items), m, GROUP,
+                                                            _OUT_CODES[out_dtype], _stream(items[0][0])))
+    return outs
+
+
+def prepared_gemv_grouped(items, out_dtype=torch.bfloat16):
+    """prepare() for w4a8_gemv_grouped: the descriptor array is built and checked once."""
+    w4a8_gemv_grouped(items, out_dtype)                      # validates and runs once
+    arr, _, m = _group_descs(items, out_dtype)
+    c, dev, n = load().w4a8_gemv_grouped, items[0][0].device, len(items)
+    code = _OUT_CODES[out_dtype]
+
+    def run():
+        st = c(ctypes.addressof(arr), n, m, GROUP, code, torch.cuda.current_stream(dev).cuda_stream)
+        if st:
+            _check("w4a8_gemv_grouped", st)
+    run.descs = arr   # keeps the array alive with the callable
+    return run
 
 
 def quantize_w4(w: torch.Tensor, codebook=None, rotated: bool = False, bias=None) -> W4A8Layer:

@@ -133,6 +133,39 @@ int w4a8_gemv(const int8_t* xq, const float* xs, int64_t M,
               int32_t out_type, void* out, void* stream);
 
 /*
+ * w4a8_gemv_grouped -- w4a8_gemv for several independent layers in as few launches as
+ * possible (32 layers per launch): the decode path of ai-toolkit w4a8_gemv_kernel for
+ * each layer, with the per-launch latency paid once per 32 layers instead of once per
+ * layer.  Every layer's output is bit-identical to a w4a8_gemv call on it.
+ *
+ *   layers    in   HOST array of `count` descriptors (read during the call only); each
+ *                  names one layer's activations (xq [M, K], xs [M]), storage, optional
+ *                  bias, output [M, N] and sizes, with the same meaning and alignment
+ *                  rules as the arguments of w4a8_gemv.  Outputs must not overlap.
+ *   count          number of layers, >= 0 (0 does nothing)
+ *   M              rows per layer, common to all layers, 0..W4A8_GEMV_MAX_M
+ *   group          must be 16
+ *   out_type       common output type
+ * The sum of N over the layers must not exceed 2^30.  Any invalid descriptor rejects
+ * the whole call before anything is launched.
+ */
+typedef struct w4a8_gemv_layer {
+    const int8_t* xq;
+    const float* xs;
+    const uint8_t* qpacked;
+    const uint8_t* srel;
+    const float* codebook;
+    const float* s_channel;
+    const float* bias;   /* or NULL */
+    void* out;
+    int64_t N;
+    int64_t K;
+} w4a8_gemv_layer;
+
+int w4a8_gemv_grouped(const w4a8_gemv_layer* layers, int32_t count, int64_t M, int32_t group,
+                      int32_t out_type, void* stream);
+
+/*
  * quantize_w4 -- the weight quantiser: an fp32 weight to the layer storage above.
  *
  * ai-toolkit ConvRotW4A8Quantizer.quantize_ (the weight is first rotated like the

@@ -27,10 +27,10 @@ def w4a8():
 
 def test_header_declares_the_operations():
     names = _declared_functions()
-    for n in ("rotate_quant_act", "decode_w4_to_int8", "w4a8_gemm", "w4a8_gemv", "quantize_w4",
-              "w4a8_status_string", "w4a8_abi_version"):
+    for n in ("rotate_quant_act", "decode_w4_to_int8", "w4a8_gemm", "w4a8_gemv", "w4a8_gemv_grouped",
+              "quantize_w4", "w4a8_status_string", "w4a8_abi_version"):
         assert n in names
-    assert len(names) == 7, names
+    assert len(names) == 8, names
 
 
 def test_library_exports_every_declared_symbol(w4a8):
@@ -45,7 +45,7 @@ def test_status_strings(w4a8):
         "W4A8_OK", "W4A8_ERR_INVALID_ARG", "W4A8_ERR_SHAPE", "W4A8_ERR_ALIGN", "W4A8_ERR_UNSUPPORTED",
         "W4A8_ERR_HIP"]
     assert w4a8.status_string(99) == "W4A8_ERR_UNKNOWN"
-    assert w4a8.load().w4a8_abi_version() == w4a8.ABI_VERSION == 2
+    assert w4a8.load().w4a8_abi_version() == w4a8.ABI_VERSION == 3
 
 
 A = 1 << 20          # a 16-byte-aligned fake address (never dereferenced: validation fails first)
@@ -119,6 +119,29 @@ def test_quantize_validation(w4a8):
         assert c(**{p: None}) == w4a8.ERR_INVALID_ARG, p
     assert c(w=A + 4) == w4a8.ERR_ALIGN and c(qp=A + 8) == w4a8.ERR_ALIGN and c(srel=A + 1) == w4a8.ERR_ALIGN
     assert c(cb=A + 2) == w4a8.ERR_ALIGN and c(sch=A + 2) == w4a8.ERR_ALIGN
+
+
+def test_gemv_grouped_validation(w4a8):
+    def desc(**kw):
+        d = dict(xq=A, xs=A, qpacked=A, srel=A, codebook=A, s_channel=A, bias=None, out=A, N=64, K=256)
+        d.update(kw)
+        return w4a8.GemvLayerDesc(**d)
+
+    def c(descs, count=None, M=1, group=16, out_type=0):
+        arr = (w4a8.GemvLayerDesc * max(len(descs), 1))(*descs)
+        return w4a8.call("w4a8_gemv_grouped", ctypes.addressof(arr), len(descs) if count is None else count, M,
+                         group, out_type, None)
+    assert ctypes.sizeof(w4a8.GemvLayerDesc) == 80
+    assert c([]) == w4a8.OK and c([desc()], M=0) == w4a8.OK and c([desc()], count=0) == w4a8.OK
+    assert c([desc()], count=-1) == w4a8.ERR_INVALID_ARG and c([desc()], M=-1) == w4a8.ERR_INVALID_ARG
+    assert c([desc()], M=9) == w4a8.ERR_UNSUPPORTED and c([desc()], group=8) == w4a8.ERR_UNSUPPORTED
+    assert c([desc()], out_type=5) == w4a8.ERR_INVALID_ARG
+    assert w4a8.call("w4a8_gemv_grouped", None, 2, 1, 16, 0, None) == w4a8.ERR_INVALID_ARG
+    # one bad descriptor among good ones rejects the whole call
+    assert c([desc(), desc(K=300), desc()]) == w4a8.ERR_SHAPE
+    assert c([desc(), desc(out=A + 8)]) == w4a8.ERR_ALIGN
+    assert c([desc(), desc(srel=None)]) == w4a8.ERR_INVALID_ARG
+    assert c([desc(N=1 << 29), desc(N=(1 << 29) + 1)]) == w4a8.ERR_SHAPE      # total rows above 2^30
 
 
 def test_binding_rejects_cpu_tensors(w4a8):
