@@ -78,25 +78,30 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
                                           const uint8_t* __restrict__ qp, const uint8_t* __restrict__ srel,
                                           const float* __restrict__ codebook, const float* __restrict__ ws,
                                           const float* __restrict__ bias, int N, int K, int out_type,
-                                          void* __restrict__ out, int block) {
+                                          void* __restrict__ out, int tile0, int ntile) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint32_t* lut = reinterpret_cast<uint32_t*>(smem);
     uint8_t* act = smem + 4096;
     const uint4* lut4 = reinterpret_cast<const uint4*>(lut);
     constexpr int SLAB = slab_cols(MM);
+    constexpr int WAVES = GV_THREADS / 64;
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n0 = (block * (GV_THREADS / 64) + wave) * R;
     const int KH = K >> 1, G = K >> 4, nchunk = K >> 4;
+    const int nbatch = (nchunk + 64 * GV_BATCH - 1) / (64 * GV_BATCH);
 
+    // tile t covers rows 4R*t .. 4R*t + 4R - 1; wave w takes R consecutive rows of it
     const uint8_t* qrow[R];
     const uint8_t* srow[R];
+    auto row_ptrs = [&](int tile, const uint8_t* (&qr)[R], const uint8_t* (&sr)[R]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int n = min(n0 + r, N - 1);
-        qrow[r] = qp + (int64_t)n * KH;
-        srow[r] = srel + (int64_t)n * G;
-    }
+        for (int r = 0; r < R; ++r) {
+            const int n = min((tile * WAVES + wave) * R + r, N - 1);
+            qr[r] = qp + (int64_t)n * KH;
+            sr[r] = srel + (int64_t)n * G;
+        }
+    };
+    row_ptrs(tile0, qrow, srow);
 
     // first batch in flight before the table build and the activation staging
     Batch<R> cur, nxt;
@@ -106,76 +111,93 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
     build_level_table(lut, codebook, threadIdx.x, GV_THREADS);
     __syncthreads();
 
-    int32_t acc[R * MM];
-#pragma unroll
-    for (int i = 0; i < R * MM; ++i) acc[i] = 0;
-
-    const int nbatch = (nchunk + 64 * GV_BATCH - 1) / (64 * GV_BATCH);
     int slab_k0 = 0;
-    for (int b = 0; b < nbatch; ++b) {
-        const int kb = b * 64 * GV_BATCH * 16;          // first column of this batch
-        if (kb >= slab_k0 + SLAB) {                      // next slab of activations (uniform branch)
-            slab_k0 += SLAB;
-            __syncthreads();
-            const int cols = K - slab_k0 < SLAB ? K - slab_k0 : SLAB;
-            stage_acts<MM>(act, xq, K, slab_k0, cols);
-            __syncthreads();
-        }
-        if (b + 1 < nbatch) load_batch<R>(nxt, qrow, srow, lane + (b + 1) * 64 * GV_BATCH, nchunk);
+    for (int t = 0; t < ntile; ++t) {
+        const int n0 = ((tile0 + t) * WAVES + wave) * R;
+        int32_t acc[R * MM];
 #pragma unroll
-        for (int u = 0; u < GV_BATCH; ++u) {
-            const int j = lane + (b * GV_BATCH + u) * 64;
-            if (j < nchunk) {
-                uint4 a[MM];
+        for (int i = 0; i < R * MM; ++i) acc[i] = 0;
+        const uint8_t* qnext[R];
+        const uint8_t* snext[R];
+        for (int b = 0; b < nbatch; ++b) {
+            const int kb = b * 64 * GV_BATCH * 16;          // first column of this batch
+            if (kb >= slab_k0 + SLAB || kb < slab_k0) {      // other slab of activations (uniform branch)
+                slab_k0 = kb - kb % SLAB;
+                __syncthreads();
+                const int cols = K - slab_k0 < SLAB ? K - slab_k0 : SLAB;
+                stage_acts<MM>(act, xq, K, slab_k0, cols);
+                __syncthreads();
+            }
+            // prefetch: the next batch of this tile, or the first batch of the next tile
+            const bool more = b + 1 < nbatch;
+            if (more) {
+                load_batch<R>(nxt, qrow, srow, lane + (b + 1) * 64 * GV_BATCH, nchunk);
+            } else if (t + 1 < ntile) {
+                row_ptrs(tile0 + t + 1, qnext, snext);
+                load_batch<R>(nxt, qnext, snext, lane, nchunk);
+            }
 #pragma unroll
-                for (int m = 0; m < MM; ++m)
-                    a[m] = *reinterpret_cast<const uint4*>(act + m * SLAB + (j * 16 - slab_k0));
+            for (int u = 0; u < GV_BATCH; ++u) {
+                const int j = lane + (b * GV_BATCH + u) * 64;
+                if (j < nchunk) {
+                    uint4 a[MM];
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const uint4 t = lut4[cur.s[u][r]];
-                    const uint2 d0 = decode8(cur.q[u][r].x, t), d1 = decode8(cur.q[u][r].y, t);
+                    for (int m = 0; m < MM; ++m)
+                        a[m] = *reinterpret_cast<const uint4*>(act + m * SLAB + (j * 16 - slab_k0));
 #pragma unroll
-                    for (int m = 0; m < MM; ++m) {
-                        int32_t s = acc[r * MM + m];
-                        s = __builtin_amdgcn_sdot4((int)d0.x, (int)a[m].x, s, false);
-                        s = __builtin_amdgcn_sdot4((int)d0.y, (int)a[m].y, s, false);
-                        s = __builtin_amdgcn_sdot4((int)d1.x, (int)a[m].z, s, false);
-                        s = __builtin_amdgcn_sdot4((int)d1.y, (int)a[m].w, s, false);
-                        acc[r * MM + m] = s;
+                    for (int r = 0; r < R; ++r) {
+                        const uint4 tt = lut4[cur.s[u][r]];
+                        const uint2 d0 = decode8(cur.q[u][r].x, tt), d1 = decode8(cur.q[u][r].y, tt);
+#pragma unroll
+                        for (int m = 0; m < MM; ++m) {
+                            int32_t sacc = acc[r * MM + m];
+                            sacc = __builtin_amdgcn_sdot4((int)d0.x, (int)a[m].x, sacc, false);
+                            sacc = __builtin_amdgcn_sdot4((int)d0.y, (int)a[m].y, sacc, false);
+                            sacc = __builtin_amdgcn_sdot4((int)d1.x, (int)a[m].z, sacc, false);
+                            sacc = __builtin_amdgcn_sdot4((int)d1.y, (int)a[m].w, sacc, false);
+                            acc[r * MM + m] = sacc;
+                        }
                     }
                 }
             }
+            if (more || t + 1 < ntile) cur = nxt;
         }
-        if (b + 1 < nbatch) cur = nxt;
-    }
-
-    // reduce-scatter of the V = R*MM partial sums over the 64 lanes: after the
-    // halving steps lane l holds value l >> (6 - L) summed over its 2^(6-L) group
-    constexpr int V = R * MM, VP = pow2_ceil(V), L = log2i(VP);
-    static_assert(VP <= 64, "too many partial sums per wave");
-    int32_t v[VP];
+        if (t + 1 < ntile) {
 #pragma unroll
-    for (int i = 0; i < VP; ++i) v[i] = i < V ? acc[i] : 0;
-#pragma unroll
-    for (int s = 0; s < L; ++s) {
-        const int o = 32 >> s, half = VP >> (s + 1);
-        const bool hi = (lane & o) != 0;
-#pragma unroll
-        for (int i = 0; i < half; ++i) {
-            const int32_t keep = hi ? v[i + half] : v[i];
-            const int32_t send = hi ? v[i] : v[i + half];
-            v[i] = keep + __shfl_xor(send, o, 64);
+            for (int r = 0; r < R; ++r) {
+                qrow[r] = qnext[r];
+                srow[r] = snext[r];
+            }
         }
-    }
-#pragma unroll
-    for (int o = 32 >> L; o >= 1; o >>= 1) v[0] += __shfl_xor(v[0], o, 64);
 
-    const int idx = lane >> (6 - L);
-    if ((lane & ((1 << (6 - L)) - 1)) == 0 && idx < V) {
-        const int r = idx / MM, m = idx - r * MM, n = n0 + r;
-        if (n < N) {
-            const float y = epilogue_f32(v[0], xs[m], ws[n], bias, n);
-            store_out(out, out_type, (int64_t)m * N + n, v[0], y);
+        // reduce-scatter of the V = R*MM partial sums over the 64 lanes: after the
+        // halving steps lane l holds value l >> (6 - L) summed over its 2^(6-L) group
+        constexpr int V = R * MM, VP = pow2_ceil(V), L = log2i(VP);
+        static_assert(VP <= 64, "too many partial sums per wave");
+        int32_t v[VP];
+#pragma unroll
+        for (int i = 0; i < VP; ++i) v[i] = i < V ? acc[i] : 0;
+#pragma unroll
+        for (int st = 0; st < L; ++st) {
+            const int o = 32 >> st, half = VP >> (st + 1);
+            const bool hi = (lane & o) != 0;
+#pragma unroll
+            for (int i = 0; i < half; ++i) {
+                const int32_t keep = hi ? v[i + half] : v[i];
+                const int32_t send = hi ? v[i] : v[i + half];
+                v[i] = keep + __shfl_xor(send, o, 64);
+            }
+        }
+#pragma unroll
+        for (int o = 32 >> L; o >= 1; o >>= 1) v[0] += __shfl_xor(v[0], o, 64);
+
+        const int idx = lane >> (6 - L);
+        if ((lane & ((1 << (6 - L)) - 1)) == 0 && idx < V) {
+            const int r = idx / MM, m = idx - r * MM, n = n0 + r;
+            if (n < N) {
+                const float y = epilogue_f32(v[0], xs[m], ws[n], bias, n);
+                store_out(out, out_type, (int64_t)m * N + n, v[0], y);
+            }
         }
     }
 }
@@ -188,14 +210,17 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(const int8_t* __restri
                                                           const float* __restrict__ ws,
                                                           const float* __restrict__ bias, int N, int K,
                                                           int out_type, void* __restrict__ out) {
-    gemv_body<MM, R>(xq, xs, qp, srel, codebook, ws, bias, N, K, out_type, out, blockIdx.x);
+    gemv_body<MM, R>(xq, xs, qp, srel, codebook, ws, bias, N, K, out_type, out, blockIdx.x, 1);
 }
 
 // Several independent layers (same M) in one launch: block b works on the layer whose
-// range [first[l], first[l+1]) of block ids holds b, as block b - first[l] of it.  The
-// layer table travels in the kernel arguments.
+// range [first[l], first[l+1]) of block ids holds b, as block b - first[l] of it, on
+// tiles_per_block consecutive row tiles (the level table and the activations are staged
+// once per block; the first loads of a tile are issued during the last batch of the
+// previous one).  The layer table travels in the kernel arguments.
 struct GroupArgs {
     int count;
+    int tiles_per_block;
     int first[GEMV_GROUP_MAX + 1];
     w4a8_gemv_layer layer[GEMV_GROUP_MAX];
 };
@@ -205,8 +230,12 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_grouped_kernel(const GroupArg
     int l = 0;
     while (l + 1 < args.count && (int)blockIdx.x >= args.first[l + 1]) ++l;   // uniform: a few steps
     const w4a8_gemv_layer& L = args.layer[l];
+    const int per_tile = (GV_THREADS / 64) * R;
+    const int tiles = (int)((L.N + per_tile - 1) / per_tile);
+    const int tile0 = ((int)blockIdx.x - args.first[l]) * args.tiles_per_block;
+    const int ntile = min(args.tiles_per_block, tiles - tile0);
     gemv_body<MM, R>(L.xq, L.xs, L.qpacked, L.srel, L.codebook, L.s_channel, L.bias, (int)L.N, (int)L.K,
-                     out_type, L.out, blockIdx.x - args.first[l]);
+                     out_type, L.out, tile0, ntile);
 }
 
 // rows per wave: as many as keep >= 2048 waves in the grid (8 per compute unit), at most 4
@@ -220,14 +249,22 @@ template <int MM>
 hipError_t launch_gemv_grouped_m(const w4a8_gemv_layer* layers, int count, int out_type, hipStream_t stream) {
     int64_t rows = 0;
     for (int i = 0; i < count; ++i) rows += layers[i].N;
-    const int R = rows_per_wave(rows), per_block = (GV_THREADS / 64) * R;
+    // at most 2 rows per wave: with several tiles per block the 4-row form needs so many
+    // registers that only one wave fits per SIMD
+    const int R = rows_per_wave(rows) < 2 ? rows_per_wave(rows) : 2, per_tile = (GV_THREADS / 64) * R;
+    // consecutive row tiles per block: enough blocks for a few rounds over the chip
+    // (256 compute units x 3 resident blocks x 4), fewer level-table builds per row
+    const int64_t total_tiles = (rows + per_tile - 1) / per_tile + count;
+    const int tpb = (int)(total_tiles / 3072 > 1 ? total_tiles / 3072 : 1);
     for (int base = 0; base < count; base += GEMV_GROUP_MAX) {
         GroupArgs a;
         a.count = count - base < GEMV_GROUP_MAX ? count - base : GEMV_GROUP_MAX;
+        a.tiles_per_block = tpb;
         a.first[0] = 0;
         for (int i = 0; i < a.count; ++i) {
             a.layer[i] = layers[base + i];
-            a.first[i + 1] = a.first[i] + (int)((layers[base + i].N + per_block - 1) / per_block);
+            const int tiles = (int)((layers[base + i].N + per_tile - 1) / per_tile);
+            a.first[i + 1] = a.first[i] + (tiles + tpb - 1) / tpb;
         }
         for (int i = a.count; i < GEMV_GROUP_MAX; ++i) a.first[i + 1] = a.first[a.count];
         const size_t lds = 4096 + (size_t)MM * slab_cols(MM);
