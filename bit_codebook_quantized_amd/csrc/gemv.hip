@@ -24,6 +24,8 @@
 // registers for the whole of K and are combined across the wave once, by a
 // reduce-scatter (each halving step exchanges half the values), so a lane ends
 // with one fully summed output.
+#include <type_traits>
+
 #include "../../include/w4a8.h"
 #include "w4a8_device.hpp"
 
@@ -46,18 +48,18 @@ struct Batch {
     uint32_t s[GV_BATCH][R];
 };
 
+// Loads are unconditional (slots past the row end re-read its last group), so the
+// compiler can count the loads in flight and wait for exactly the batch it needs.
 template <int R>
 __device__ __forceinline__ void load_batch(Batch<R>& b, const uint8_t* const (&qrow)[R], const uint8_t* const (&srow)[R],
                                            int jbase, int nchunk) {
 #pragma unroll
     for (int u = 0; u < GV_BATCH; ++u) {
-        const int j = jbase + 64 * u;
-        if (j < nchunk) {
+        const int j = min(jbase + 64 * u, nchunk - 1);
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                b.q[u][r] = *reinterpret_cast<const uint2*>(qrow[r] + (int64_t)j * 8);
-                b.s[u][r] = srow[r][j];
-            }
+        for (int r = 0; r < R; ++r) {
+            b.q[u][r] = *reinterpret_cast<const uint2*>(qrow[r] + (int64_t)j * 8);
+            b.s[u][r] = srow[r][j];
         }
     }
 }
@@ -86,120 +88,143 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
     constexpr int SLAB = slab_cols(MM);
     constexpr int WAVES = GV_THREADS / 64;
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wave index as a uniform value, so row-dependent scalars use scalar loads
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int KH = K >> 1, G = K >> 4, nchunk = K >> 4;
-    const int nbatch = (nchunk + 64 * GV_BATCH - 1) / (64 * GV_BATCH);
-
-    // tile t covers rows 4R*t .. 4R*t + 4R - 1; wave w takes R consecutive rows of it
-    const uint8_t* qrow[R];
-    const uint8_t* srow[R];
-    auto row_ptrs = [&](int tile, const uint8_t* (&qr)[R], const uint8_t* (&sr)[R]) __attribute__((always_inline)) {
+    // the work is a sequence of steps (tile t, batch gb): batch gb covers groups
+    // 256*gb .. 256*gb + 255 of each of the tile's rows; tile t covers rows
+    // 4R*(tile0 + t) ..; wave w takes R consecutive rows of it
+    const int nbt = (nchunk + 64 * GV_BATCH - 1) / (64 * GV_BATCH);
+    const int nsteps = ntile * nbt;
+    auto issue = [&](Batch<R>& dst, int step) __attribute__((always_inline)) {
+        step = min(step, nsteps - 1);   // past the end: a harmless reload of the last step
+        const int t = step / nbt, gb = step - t * nbt;
+        const uint8_t* qr[R];
+        const uint8_t* sr[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int n = min((tile * WAVES + wave) * R + r, N - 1);
+            const int n = min(((tile0 + t) * WAVES + wave) * R + r, N - 1);
             qr[r] = qp + (int64_t)n * KH;
             sr[r] = srel + (int64_t)n * G;
         }
+        load_batch<R>(dst, qr, sr, lane + gb * 64 * GV_BATCH, nchunk);
     };
-    row_ptrs(tile0, qrow, srow);
 
     // first batch in flight before the table build and the activation staging
-    Batch<R> cur, nxt;
-    load_batch<R>(cur, qrow, srow, lane, nchunk);
+    Batch<R> bA, bB;
+    issue(bA, 0);
     const int cols0 = K < SLAB ? K : SLAB;
     stage_acts<MM>(act, xq, K, 0, cols0);
     build_level_table(lut, codebook, threadIdx.x, GV_THREADS);
     __syncthreads();
 
-    int slab_k0 = 0;
-    for (int t = 0; t < ntile; ++t) {
-        const int n0 = ((tile0 + t) * WAVES + wave) * R;
-        int32_t acc[R * MM];
+    float xsr[MM];   // the rows' activation scales, for the epilogue
 #pragma unroll
-        for (int i = 0; i < R * MM; ++i) acc[i] = 0;
-        const uint8_t* qnext[R];
-        const uint8_t* snext[R];
-        for (int b = 0; b < nbatch; ++b) {
-            const int kb = b * 64 * GV_BATCH * 16;          // first column of this batch
-            if (kb >= slab_k0 + SLAB || kb < slab_k0) {      // other slab of activations (uniform branch)
-                slab_k0 = kb - kb % SLAB;
+    for (int m = 0; m < MM; ++m) xsr[m] = xs[m];
+    int32_t acc[R * MM];
+    int slab_k0 = 0;
+
+    // One step: prefetch the next step's batch into `nxt` (unconditionally, so the compiler
+    // can count the loads in flight), multiply-accumulate `cur`, and finish the tile after
+    // its last batch.  `live` is false only for the padding step of an odd count, which
+    // only issues its (harmless) prefetch.
+    auto body = [&](int step, const Batch<R>& cur, Batch<R>& nxt, bool live, auto one_slab, auto prefetch)
+                    __attribute__((always_inline)) {
+        constexpr bool ONE = decltype(one_slab)::value;
+        if (decltype(prefetch)::value) issue(nxt, step + 1);
+        if (!live) return;   // the padding step only keeps the load count even
+        const int t = step / nbt, gb = step - t * nbt;
+        if (gb == 0) {
+#pragma unroll
+            for (int i = 0; i < R * MM; ++i) acc[i] = 0;
+        }
+        if (!ONE) {
+            const int k0 = (gb * 64 * GV_BATCH * 16 / SLAB) * SLAB;
+            if (k0 != slab_k0) {                 // other slab of activations (uniform)
+                slab_k0 = k0;
                 __syncthreads();
                 const int cols = K - slab_k0 < SLAB ? K - slab_k0 : SLAB;
                 stage_acts<MM>(act, xq, K, slab_k0, cols);
                 __syncthreads();
             }
-            // prefetch: the next batch of this tile, or the first batch of the next tile
-            const bool more = b + 1 < nbatch;
-            if (more) {
-                load_batch<R>(nxt, qrow, srow, lane + (b + 1) * 64 * GV_BATCH, nchunk);
-            } else if (t + 1 < ntile) {
-                row_ptrs(tile0 + t + 1, qnext, snext);
-                load_batch<R>(nxt, qnext, snext, lane, nchunk);
-            }
+        }
 #pragma unroll
-            for (int u = 0; u < GV_BATCH; ++u) {
-                const int j = lane + (b * GV_BATCH + u) * 64;
-                if (j < nchunk) {
-                    uint4 a[MM];
+        for (int u = 0; u < GV_BATCH; ++u) {
+            const int j = lane + (gb * GV_BATCH + u) * 64;
+            if (j < nchunk) {
+                uint4 a[MM];
 #pragma unroll
-                    for (int m = 0; m < MM; ++m)
-                        a[m] = *reinterpret_cast<const uint4*>(act + m * SLAB + (j * 16 - slab_k0));
+                for (int m = 0; m < MM; ++m)
+                    a[m] = *reinterpret_cast<const uint4*>(act + m * SLAB + (j * 16 - slab_k0));
 #pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const uint4 tt = lut4[cur.s[u][r]];
-                        const uint2 d0 = decode8(cur.q[u][r].x, tt), d1 = decode8(cur.q[u][r].y, tt);
+                for (int r = 0; r < R; ++r) {
+                    const uint4 tt = lut4[cur.s[u][r]];
+                    const uint2 d0 = decode8(cur.q[u][r].x, tt), d1 = decode8(cur.q[u][r].y, tt);
 #pragma unroll
-                        for (int m = 0; m < MM; ++m) {
-                            int32_t sacc = acc[r * MM + m];
-                            sacc = __builtin_amdgcn_sdot4((int)d0.x, (int)a[m].x, sacc, false);
-                            sacc = __builtin_amdgcn_sdot4((int)d0.y, (int)a[m].y, sacc, false);
-                            sacc = __builtin_amdgcn_sdot4((int)d1.x, (int)a[m].z, sacc, false);
-                            sacc = __builtin_amdgcn_sdot4((int)d1.y, (int)a[m].w, sacc, false);
-                            acc[r * MM + m] = sacc;
-                        }
+                    for (int m = 0; m < MM; ++m) {
+                        int32_t sacc = acc[r * MM + m];
+                        sacc = __builtin_amdgcn_sdot4((int)d0.x, (int)a[m].x, sacc, false);
+                        sacc = __builtin_amdgcn_sdot4((int)d0.y, (int)a[m].y, sacc, false);
+                        sacc = __builtin_amdgcn_sdot4((int)d1.x, (int)a[m].z, sacc, false);
+                        sacc = __builtin_amdgcn_sdot4((int)d1.y, (int)a[m].w, sacc, false);
+                        acc[r * MM + m] = sacc;
                     }
                 }
             }
-            if (more || t + 1 < ntile) cur = nxt;
         }
-        if (t + 1 < ntile) {
+        if (gb == nbt - 1) {
+            // reduce-scatter of the V = R*MM partial sums over the 64 lanes: after the
+            // halving steps lane l holds value l >> (6 - L) summed over its 2^(6-L) group
+            constexpr int V = R * MM, VP = pow2_ceil(V), L = log2i(VP);
+            static_assert(VP <= 64, "too many partial sums per wave");
+            int32_t v[VP];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                qrow[r] = qnext[r];
-                srow[r] = snext[r];
+            for (int i = 0; i < VP; ++i) v[i] = i < V ? acc[i] : 0;
+#pragma unroll
+            for (int st = 0; st < L; ++st) {
+                const int o = 32 >> st, half = VP >> (st + 1);
+                const bool hi = (lane & o) != 0;
+#pragma unroll
+                for (int i = 0; i < half; ++i) {
+                    const int32_t keep = hi ? v[i + half] : v[i];
+                    const int32_t send = hi ? v[i] : v[i + half];
+                    v[i] = keep + __shfl_xor(send, o, 64);
+                }
             }
-        }
+#pragma unroll
+            for (int o = 32 >> L; o >= 1; o >>= 1) v[0] += __shfl_xor(v[0], o, 64);
 
-        // reduce-scatter of the V = R*MM partial sums over the 64 lanes: after the
-        // halving steps lane l holds value l >> (6 - L) summed over its 2^(6-L) group
-        constexpr int V = R * MM, VP = pow2_ceil(V), L = log2i(VP);
-        static_assert(VP <= 64, "too many partial sums per wave");
-        int32_t v[VP];
+            const int n0 = ((tile0 + t) * WAVES + wave) * R;
+            const int idx = lane >> (6 - L);
+            const int r = idx / MM, m = idx - r * MM;
+            // per-row epilogue operands: wave-uniform addresses (scalar loads)
+            float wn = ws[min(n0, N - 1)], bn = bias ? bias[min(n0, N - 1)] : 0.0f;
 #pragma unroll
-        for (int i = 0; i < VP; ++i) v[i] = i < V ? acc[i] : 0;
-#pragma unroll
-        for (int st = 0; st < L; ++st) {
-            const int o = 32 >> st, half = VP >> (st + 1);
-            const bool hi = (lane & o) != 0;
-#pragma unroll
-            for (int i = 0; i < half; ++i) {
-                const int32_t keep = hi ? v[i + half] : v[i];
-                const int32_t send = hi ? v[i] : v[i + half];
-                v[i] = keep + __shfl_xor(send, o, 64);
+            for (int i = 1; i < R; ++i) {
+                const float wi = ws[min(n0 + i, N - 1)], bi = bias ? bias[min(n0 + i, N - 1)] : 0.0f;
+                wn = r == i ? wi : wn;
+                bn = r == i ? bi : bn;
             }
-        }
+            float xm = xsr[0];
 #pragma unroll
-        for (int o = 32 >> L; o >= 1; o >>= 1) v[0] += __shfl_xor(v[0], o, 64);
-
-        const int idx = lane >> (6 - L);
-        if ((lane & ((1 << (6 - L)) - 1)) == 0 && idx < V) {
-            const int r = idx / MM, m = idx - r * MM, n = n0 + r;
-            if (n < N) {
-                const float y = epilogue_f32(v[0], xs[m], ws[n], bias, n);
+            for (int i = 1; i < MM; ++i) xm = m == i ? xsr[i] : xm;
+            const int n = n0 + r;
+            if ((lane & ((1 << (6 - L)) - 1)) == 0 && idx < V && n < N) {
+                float y = __fmul_rn((float)v[0], __fmul_rn(xm, wn));
+                if (bias) y = __fadd_rn(y, bn);
                 store_out(out, out_type, (int64_t)m * N + n, v[0], y);
             }
         }
-    }
+    };
+    auto run = [&](auto one_slab) __attribute__((always_inline)) {
+        for (int step = 0; step < nsteps; step += 2) {   // ping-pong: no register copies
+            body(step, bA, bB, true, one_slab, std::true_type{});
+            body(step + 1, bB, bA, step + 1 < nsteps, one_slab, std::true_type{});
+        }
+    };
+    if (nsteps == 1) body(0, bA, bB, true, std::true_type{}, std::false_type{});   // one tile, one batch
+    else if (K <= SLAB) run(std::true_type{});
+    else run(std::false_type{});
 }
 
 template <int MM, int R>
@@ -238,20 +263,15 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_grouped_kernel(const GroupArg
                      out_type, L.out, tile0, ntile);
 }
 
-// rows per wave: as many as keep >= 2048 waves in the grid (8 per compute unit), at most 4
-int rows_per_wave(int64_t rows) {
-    int R = 4;
-    while (R > 1 && (rows + R - 1) / R < 2048) R >>= 1;
-    return R;
-}
+// rows per wave: 2 when that still gives >= 2048 waves (8 per compute unit), else 1
+// (4 rows per wave would need so many registers that few waves fit per SIMD)
+int rows_per_wave(int64_t rows) { return (rows + 1) / 2 >= 2048 ? 2 : 1; }
 
 template <int MM>
 hipError_t launch_gemv_grouped_m(const w4a8_gemv_layer* layers, int count, int out_type, hipStream_t stream) {
     int64_t rows = 0;
     for (int i = 0; i < count; ++i) rows += layers[i].N;
-    // at most 2 rows per wave: with several tiles per block the 4-row form needs so many
-    // registers that only one wave fits per SIMD
-    const int R = rows_per_wave(rows) < 2 ? rows_per_wave(rows) : 2, per_tile = (GV_THREADS / 64) * R;
+    const int R = rows_per_wave(rows), per_tile = (GV_THREADS / 64) * R;
     // consecutive row tiles per block: enough blocks for a few rounds over the chip
     // (256 compute units x 3 resident blocks x 4), fewer level-table builds per row
     const int64_t total_tiles = (rows + per_tile - 1) / per_tile + count;
@@ -269,9 +289,7 @@ hipError_t launch_gemv_grouped_m(const w4a8_gemv_layer* layers, int count, int o
         for (int i = a.count; i < GEMV_GROUP_MAX; ++i) a.first[i + 1] = a.first[a.count];
         const size_t lds = 4096 + (size_t)MM * slab_cols(MM);
         const dim3 g(a.first[a.count]), b(GV_THREADS);
-        if (R == 4)
-            hipLaunchKernelGGL((gemv_grouped_kernel<MM, 4>), g, b, lds, stream, a, out_type);
-        else if (R == 2)
+        if (R == 2)
             hipLaunchKernelGGL((gemv_grouped_kernel<MM, 2>), g, b, lds, stream, a, out_type);
         else
             hipLaunchKernelGGL((gemv_grouped_kernel<MM, 1>), g, b, lds, stream, a, out_type);
@@ -290,10 +308,7 @@ hipError_t launch_gemv_m(const int8_t* xq, const float* xs, const uint8_t* qp, c
     const int blocks = (N + waves_per_block * R - 1) / (waves_per_block * R);
     const size_t lds = 4096 + (size_t)MM * slab_cols(MM);
     const dim3 g(blocks), b(GV_THREADS);
-    if (R == 4)
-        hipLaunchKernelGGL((gemv_kernel<MM, 4>), g, b, lds, stream, xq, xs, qp, srel, codebook, ws, bias, N, K,
-                           out_type, out);
-    else if (R == 2)
+    if (R == 2)
         hipLaunchKernelGGL((gemv_kernel<MM, 2>), g, b, lds, stream, xq, xs, qp, srel, codebook, ws, bias, N, K,
                            out_type, out);
     else
