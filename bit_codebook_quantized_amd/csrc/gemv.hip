@@ -116,11 +116,12 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
     const int cols0 = K < SLAB ? K : SLAB;
     stage_acts<MM>(act, xq, K, 0, cols0);
     build_level_table(lut, codebook, threadIdx.x, GV_THREADS);
+    // the rows' activation scales, for the epilogue (in LDS: a lane-dependent index into a
+    // register array would put it in scratch memory)
+    if (threadIdx.x < MM) reinterpret_cast<float*>(act + MM * SLAB)[threadIdx.x] = xs[threadIdx.x];
     __syncthreads();
 
-    float xsr[MM];   // the rows' activation scales, for the epilogue
-#pragma unroll
-    for (int m = 0; m < MM; ++m) xsr[m] = xs[m];
+    const float* xs_lds = reinterpret_cast<const float*>(act + MM * SLAB);   // staged below
     int32_t acc[R * MM];
     int slab_k0 = 0;
 
@@ -205,9 +206,7 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
                 wn = r == i ? wi : wn;
                 bn = r == i ? bi : bn;
             }
-            float xm = xsr[0];
-#pragma unroll
-            for (int i = 1; i < MM; ++i) xm = m == i ? xsr[i] : xm;
+            const float xm = xs_lds[m < MM ? m : 0];
             const int n = n0 + r;
             if ((lane & ((1 << (6 - L)) - 1)) == 0 && idx < V && n < N) {
                 float y = __fmul_rn((float)v[0], __fmul_rn(xm, wn));
@@ -287,7 +286,7 @@ hipError_t launch_gemv_grouped_m(const w4a8_gemv_layer* layers, int count, int o
             a.first[i + 1] = a.first[i] + (tiles + tpb - 1) / tpb;
         }
         for (int i = a.count; i < GEMV_GROUP_MAX; ++i) a.first[i + 1] = a.first[a.count];
-        const size_t lds = 4096 + (size_t)MM * slab_cols(MM);
+        const size_t lds = 4096 + (size_t)MM * slab_cols(MM) + 32;
         const dim3 g(a.first[a.count]), b(GV_THREADS);
         if (R == 2)
             hipLaunchKernelGGL((gemv_grouped_kernel<MM, 2>), g, b, lds, stream, a, out_type);
@@ -306,7 +305,7 @@ hipError_t launch_gemv_m(const int8_t* xq, const float* xs, const uint8_t* qp, c
     const int waves_per_block = GV_THREADS / 64;
     const int R = rows_per_wave(N);
     const int blocks = (N + waves_per_block * R - 1) / (waves_per_block * R);
-    const size_t lds = 4096 + (size_t)MM * slab_cols(MM);
+    const size_t lds = 4096 + (size_t)MM * slab_cols(MM) + 32;
     const dim3 g(blocks), b(GV_THREADS);
     if (R == 2)
         hipLaunchKernelGGL((gemv_kernel<MM, 2>), g, b, lds, stream, xq, xs, qp, srel, codebook, ws, bias, N, K,
