@@ -64,15 +64,42 @@ __device__ __forceinline__ void load_batch(Batch<R>& b, const uint8_t* const (&q
     }
 }
 
-template <int MM>
-__device__ __forceinline__ void stage_acts(uint8_t* act, const int8_t* __restrict__ xq, int K, int k0, int cols) {
-    // MM rows x cols bytes of xq starting at column k0 -> act[m * cols_cap ...]
-    const int per_row = cols >> 4;   // uint4 per row
-    for (int i = threadIdx.x; i < MM * per_row; i += GV_THREADS) {
-        const int m = i / per_row, c = i - m * per_row;
-        *reinterpret_cast<uint4*>(act + m * slab_cols(MM) + c * 16) =
-            *reinterpret_cast<const uint4*>(xq + (int64_t)m * K + k0 + c * 16);
-    }
+// Activation staging: MM rows x cols bytes of xq from column k0 (cols <= slab_cols(MM))
+// -> act[m * slab_cols(MM) ...].  Every load is issued before the first wait; `between`
+// runs after the loads and before the stores (the GEMV issues its first weight batch
+// there).  NC uint4 per thread and row, a compile-time count (an index guarded by a
+// run-time test would keep the staging registers in scratch memory): chunks past the row
+// end are clamped to its last chunk and rewrite it with the same bytes.
+template <int MM, int NC, typename F>
+__device__ __forceinline__ void stage_acts_n(uint8_t* act, const int8_t* __restrict__ xq, int K, int k0, int per_row,
+                                             F&& between) {
+    uint4 v[MM][NC];
+#pragma unroll
+    for (int m = 0; m < MM; ++m)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int i = min((int)threadIdx.x + 256 * c, per_row - 1);
+            v[m][c] = *reinterpret_cast<const uint4*>(xq + (int64_t)m * K + k0 + i * 16);
+        }
+    between();
+#pragma unroll
+    for (int m = 0; m < MM; ++m)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int i = min((int)threadIdx.x + 256 * c, per_row - 1);
+            *reinterpret_cast<uint4*>(act + m * slab_cols(MM) + i * 16) = v[m][c];
+        }
+}
+
+template <int MM, typename F>
+__device__ __forceinline__ void stage_acts(uint8_t* act, const int8_t* __restrict__ xq, int K, int k0, int cols,
+                                           F&& between) {
+    constexpr int PER = slab_cols(MM) / 16 / 256;   // at most 8
+    const int per_row = cols >> 4;
+    if (per_row <= 256 || PER == 1) stage_acts_n<MM, 1>(act, xq, K, k0, per_row, between);
+    else if (per_row <= 512 || PER == 2) stage_acts_n<MM, (PER < 2 ? PER : 2)>(act, xq, K, k0, per_row, between);
+    else if (per_row <= 1024 || PER == 4) stage_acts_n<MM, (PER < 4 ? PER : 4)>(act, xq, K, k0, per_row, between);
+    else stage_acts_n<MM, PER>(act, xq, K, k0, per_row, between);
 }
 
 template <int MM, int R>
@@ -110,15 +137,20 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
         load_batch<R>(dst, qr, sr, lane + gb * 64 * GV_BATCH, nchunk);
     };
 
-    // first batch in flight before the table build and the activation staging
-    Batch<R> bA, bB;
-    issue(bA, 0);
+    // activation loads first, then the first weight batch: the wait before the activation
+    // stores (in issue order) leaves the weight loads outstanding while the level table
+    // is built from the codebook (uniform loads)
     const int cols0 = K < SLAB ? K : SLAB;
-    stage_acts<MM>(act, xq, K, 0, cols0);
-    build_level_table(lut, codebook, threadIdx.x, GV_THREADS);
+    const float xsv = xs[min((int)threadIdx.x, MM - 1)];
+    Batch<R> bA, bB;
+    stage_acts<MM>(act, xq, K, 0, cols0, [&]() __attribute__((always_inline)) { issue(bA, 0); });
     // the rows' activation scales, for the epilogue (in LDS: a lane-dependent index into a
     // register array would put it in scratch memory)
-    if (threadIdx.x < MM) reinterpret_cast<float*>(act + MM * SLAB)[threadIdx.x] = xs[threadIdx.x];
+    if (threadIdx.x < MM) reinterpret_cast<float*>(act + MM * SLAB)[threadIdx.x] = xsv;
+    float cb[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) cb[c] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(codebook[c])));
+    build_level_table_regs(lut, cb, threadIdx.x, GV_THREADS);
     __syncthreads();
 
     const float* xs_lds = reinterpret_cast<const float*>(act + MM * SLAB);   // staged below
@@ -143,9 +175,9 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
             const int k0 = (gb * 64 * GV_BATCH * 16 / SLAB) * SLAB;
             if (k0 != slab_k0) {                 // other slab of activations (uniform)
                 slab_k0 = k0;
-                __syncthreads();
                 const int cols = K - slab_k0 < SLAB ? K - slab_k0 : SLAB;
-                stage_acts<MM>(act, xq, K, slab_k0, cols);
+                __syncthreads();
+                stage_acts<MM>(act, xq, K, slab_k0, cols, []() {});
                 __syncthreads();
             }
         }
@@ -184,11 +216,15 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
 #pragma unroll
             for (int st = 0; st < L; ++st) {
                 const int o = 32 >> st, half = VP >> (st + 1);
-                const bool hi = (lane & o) != 0;
+                // lanes with bit o set keep the upper half; the swap is masked xor
+                // arithmetic on an opaque mask (a select here is folded into a
+                // lane-dependent index into v, i.e. a compare chain over all of it)
+                int32_t hm = -((lane >> (5 - st)) & 1);
+                asm volatile("" : "+v"(hm));
 #pragma unroll
                 for (int i = 0; i < half; ++i) {
-                    const int32_t keep = hi ? v[i + half] : v[i];
-                    const int32_t send = hi ? v[i] : v[i + half];
+                    const int32_t d = (v[i] ^ v[i + half]) & hm;
+                    const int32_t keep = v[i] ^ d, send = v[i + half] ^ d;
                     v[i] = keep + __shfl_xor(send, o, 64);
                 }
             }

@@ -37,6 +37,22 @@ __device__ __forceinline__ uint32_t grid_level(float level, float scale) {
 // Fill the LDS level table: lut[4*b + q] holds the levels of codes 4q..4q+3 for
 // scale byte b, one byte each (code 4q in the low byte).  All threads of the
 // block take part; the caller synchronises afterwards.
+// The same table from the 16 codebook values already in registers (uniform loads):
+// nthreads must be a multiple of 4, so a thread's level quarter q is fixed.
+__device__ __forceinline__ void build_level_table_regs(uint32_t* lut, const float (&cb)[16], int tid, int nthreads) {
+    const int q = tid & 3;
+    float c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = q == 0 ? cb[j] : q == 1 ? cb[4 + j] : q == 2 ? cb[8 + j] : cb[12 + j];
+    for (int i = tid; i < 1024; i += nthreads) {
+        const float s = e4m3fn_to_f32((uint32_t)(i >> 2));
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w |= grid_level(c[j], s) << (8 * j);
+        lut[i] = w;
+    }
+}
+
 __device__ __forceinline__ void build_level_table(uint32_t* lut, const float* __restrict__ codebook,
                                                   int tid, int nthreads) {
     for (int i = tid; i < 1024; i += nthreads) {
