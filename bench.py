@@ -163,6 +163,11 @@ def bench_gemv(args, torch, B, device):
         cold_ms, enq = timed_launches(torch, cold, args.gemv_launches, sleep)
         warm_ms, _ = timed_launches(torch, cold[:1], 64, sleep // 4)
         rq_ms, _ = timed_launches(torch, rq, 64, sleep // 4)
+        # the whole decode layer: rotate_quant_act + w4a8_gemv, and the one-launch w4a8_gemv_act
+        two = [lambda c=c: (rq[0](), cold[c]()) for c in range(copies)]
+        two_ms, _ = timed_launches(torch, two, args.gemv_launches, sleep)
+        act = [B.prepared_gemv_act(x, layers[c], out) for c in range(copies)]
+        act_ms, _ = timed_launches(torch, act, args.gemv_launches, sleep)
         wb = weight_bytes(N, K)
         res[str(m)] = dict(
             gemv_us=round(cold_ms * 1e3, 3),
@@ -172,6 +177,9 @@ def bench_gemv(args, torch, B, device):
             warm_cache_us=round(warm_ms * 1e3, 3),
             warm_cache_weight_GBps=round(wb / (warm_ms * 1e-3) / 1e9, 1),
             rotate_quant_us=round(rq_ms * 1e3, 3),
+            layer_two_launches_us=round(two_ms * 1e3, 3),
+            layer_gemv_act_us=round(act_ms * 1e3, 3),
+            layer_gemv_act_weight_GBps=round(wb / (act_ms * 1e-3) / 1e9, 1),
             host_enqueue_us=round(enq / args.gemv_launches * 1e6, 2),
         )
     return res

@@ -28,6 +28,7 @@
 
 #include "../../include/w4a8.h"
 #include "w4a8_device.hpp"
+#include "rotq_device.hpp"
 
 namespace w4a8 {
 namespace {
@@ -102,12 +103,137 @@ __device__ __forceinline__ void stage_acts(uint8_t* act, const int8_t* __restric
     else stage_acts_n<MM, PER>(act, xq, K, k0, per_row, between);
 }
 
-template <int MM, int R>
+// Bytes of dynamic LDS of a GEMV block: level table, activation slab, the rows' scales,
+// and for the fused form the rotation's transpose buffer and the row maxima.
+__host__ __device__ constexpr size_t gemv_lds_bytes(int mm, bool fused) {
+    return 4096 + (size_t)mm * slab_cols(mm) + 32 + (fused ? ROTQ_TBUF_DOUBLES * 8 + 2 * 16 * 4 : 0);
+}
+
+// The fused form's activation preparation: the block rotates and quantises the MM bf16
+// rows itself (K <= slab_cols(MM)), with the arithmetic of rotate_quant_act, into the
+// activation slab and the scale slots.  Slot s of 16 lanes rotates the 256-column blocks
+// s, s + 16, ... of a row; the row maximum is taken over the 16 slots.  The work is a
+// sequence of jobs, one 256-column block per slot each: one job per row when K <= 4096
+// (the rotated values stay in registers between the maximum and the quantisation), else
+// nch jobs for the maximum and nch jobs that rotate again and quantise.  The inputs of
+// job j + 2 are loaded while jobs j and j + 1 are computed (two named buffers, so no
+// register copy of a load in flight).  `first` holds the inputs of jobs 0 and 1, loaded
+// by the caller (rot_first_job) before anything else.  xq_out /
+// xs_out, when not null, receive the same int8 rows and scales.
+// job j's block for this lane's slot, clamped into range (out-of-range slots are zeroed)
+__device__ __forceinline__ RotIn rot_job_load(const uint16_t* __restrict__ x, int K, int j, int njobs,
+                                              int jobs_per_row, int nch) {
+    j = min(j, njobs - 1);   // past the end: a harmless reload of the last job
+    const int row = j / jobs_per_row, c = j - row * jobs_per_row;
+    const int blk = min((int)(threadIdx.x >> 4) + 16 * (c % nch), (K >> 8) - 1);
+    return rot_load(x, row, K, blk, threadIdx.x & 15);
+}
+
+__device__ __forceinline__ int rot_jobs_per_row(int K) {
+    const int nch = ((K >> 8) + 15) >> 4;
+    return nch == 1 ? 1 : 2 * nch;
+}
+
+template <int MM>
+__device__ __forceinline__ RotIn rot_first_job(const uint16_t* __restrict__ x, int K, int j) {
+    const int nch = ((K >> 8) + 15) >> 4, jpr = rot_jobs_per_row(K);
+    return rot_job_load(x, K, j, MM * jpr, jpr, nch);
+}
+
+template <int MM, bool LONGK>
+__device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds, double* tbuf, float* smax,
+                                                    const uint16_t* __restrict__ x, int K, int qmax,
+                                                    const RotIn first0, const RotIn first1,
+                                                    int8_t* __restrict__ xq_out,
+                                                    float* __restrict__ xs_out) {
+    constexpr int SLAB = slab_cols(MM);
+    const int tid = threadIdx.x, slot = tid >> 4, l16 = tid & 15;
+    const int nb = K >> 8, nch = LONGK ? (nb + 15) >> 4 : 1;   // LONGK: K > 4096
+    const int jobs_per_row = LONGK ? rot_jobs_per_row(K) : 1;
+    const int njobs = MM * jobs_per_row;
+    const float qmaxf = (float)qmax;
+    float r[16];
+    float amax = 0.0f, scale = 1.0f;
+    double inv = 1.0;
+
+    auto load_job = [&](int j) __attribute__((always_inline)) {
+        return rot_job_load(x, K, j, njobs, jobs_per_row, nch);
+    };
+    auto run_job = [&](int j, const RotIn in) __attribute__((always_inline)) {
+        const int row = j / jobs_per_row, c = j - row * jobs_per_row;
+        const bool pass1 = nch == 1 || c < nch;
+        const int cc = nch == 1 ? 0 : (pass1 ? c : c - nch);
+        const int blk = slot + 16 * cc;
+        const bool ok = blk < nb;
+        rotate_loaded(in, ok, slot, l16, tbuf, r);
+        if (pass1) {
+            if (cc == 0) amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(r[i]));
+            if (cc == nch - 1) {
+                const float a = slot_max(amax);
+                float* sm = smax + 16 * (row & 1);   // alternate rows: no barrier before the next write
+                if (l16 == 0) sm[slot] = a;
+                __syncthreads();
+                float rmax = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) rmax = __builtin_fmaxf(rmax, sm[i]);
+                scale = rmax > 0.0f ? rmax / qmaxf : 1.0f;   // IEEE fp32 division
+                inv = 1.0 / (double)scale;
+                if (tid == 0) {
+                    xs_lds[row] = scale;
+                    if (xs_out) xs_out[row] = scale;
+                }
+            }
+        }
+        if ((nch == 1 || !pass1) && ok) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) act[row * SLAB + blk * 256 + 16 * i + l16] = (uint8_t)quant1(r[i], inv, qmaxf);
+        }
+    };
+
+    RotIn bA = first0, bB = first1;
+    if constexpr (!LONGK) {
+        // K <= 4096, one job per row: straight-line code (exact wait counts for the loads
+        // in flight; a kernel holds only one of the two forms, so no merged wait state)
+#pragma unroll
+        for (int j = 0; j < MM; j += 2) {
+            run_job(j, bA);
+            if (j + 2 < MM) bA = load_job(j + 2);
+            if (j + 1 < MM) {
+                run_job(j + 1, bB);
+                if (j + 3 < MM) bB = load_job(j + 3);
+            }
+        }
+    } else {
+        for (int j = 0; j < njobs; j += 2) {
+            run_job(j, bA);
+            bA = load_job(j + 2);
+            if (j + 1 < njobs) run_job(j + 1, bB);
+            bB = load_job(j + 3);
+        }
+    }
+    if (xq_out) {   // block-uniform
+        __syncthreads();
+        const int per_row = K >> 4;
+        for (int i = tid; i < MM * per_row; i += GV_THREADS) {
+            const int m = i / per_row, c = i - m * per_row;
+            *reinterpret_cast<uint4*>(xq_out + (int64_t)m * K + c * 16) =
+                *reinterpret_cast<const uint4*>(act + m * SLAB + c * 16);
+        }
+    }
+}
+
+// FUSED: the activations arrive as bf16 rows x (rotated and quantised in the block, see
+// rotate_quant_to_lds; K <= slab_cols(MM)) instead of xq / xs.
+template <int MM, int R, bool FUSED = false, bool LONGK = false>
 __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const float* __restrict__ xs,
                                           const uint8_t* __restrict__ qp, const uint8_t* __restrict__ srel,
                                           const float* __restrict__ codebook, const float* __restrict__ ws,
                                           const float* __restrict__ bias, int N, int K, int out_type,
-                                          void* __restrict__ out, int tile0, int ntile) {
+                                          void* __restrict__ out, int tile0, int ntile,
+                                          const uint16_t* __restrict__ x = nullptr, int qmax = 127,
+                                          int8_t* __restrict__ xq_out = nullptr, float* __restrict__ xs_out = nullptr) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint32_t* lut = reinterpret_cast<uint32_t*>(smem);
     uint8_t* act = smem + 4096;
@@ -137,23 +263,38 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
         load_batch<R>(dst, qr, sr, lane + gb * 64 * GV_BATCH, nchunk);
     };
 
-    // activation loads first, then the first weight batch: the wait before the activation
-    // stores (in issue order) leaves the weight loads outstanding while the level table
-    // is built from the codebook (uniform loads)
-    const int cols0 = K < SLAB ? K : SLAB;
-    const float xsv = xs[min((int)threadIdx.x, MM - 1)];
+    float* xs_w = reinterpret_cast<float*>(act + MM * SLAB);   // the rows' activation scales
     Batch<R> bA, bB;
-    stage_acts<MM>(act, xq, K, 0, cols0, [&]() __attribute__((always_inline)) { issue(bA, 0); });
-    // the rows' activation scales, for the epilogue (in LDS: a lane-dependent index into a
-    // register array would put it in scratch memory)
-    if (threadIdx.x < MM) reinterpret_cast<float*>(act + MM * SLAB)[threadIdx.x] = xsv;
-    float cb[16];
+    if constexpr (FUSED) {
+        // the first rotation inputs, then (after a compiler barrier that keeps this issue
+        // order) the first weight batch: the rotation waits only for its own loads
+        const RotIn first0 = rot_first_job<MM>(x, K, 0), first1 = rot_first_job<MM>(x, K, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(bA, 0);
+        float cb[16];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) cb[c] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(codebook[c])));
-    build_level_table_regs(lut, cb, threadIdx.x, GV_THREADS);
+        for (int c = 0; c < 16; ++c) cb[c] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(codebook[c])));
+        build_level_table_regs(lut, cb, threadIdx.x, GV_THREADS);
+        double* tbuf = reinterpret_cast<double*>(act + MM * SLAB + 32);
+        rotate_quant_to_lds<MM, LONGK>(act, xs_w, tbuf, reinterpret_cast<float*>(tbuf + ROTQ_TBUF_DOUBLES), x, K, qmax,
+                                first0, first1, xq_out, xs_out);
+    } else {
+        // activation loads first, then the first weight batch: the wait before the
+        // activation stores leaves the weight loads outstanding while the level table
+        // is built from the codebook (uniform loads)
+        const int cols0 = K < SLAB ? K : SLAB;
+        const float xsv = xs[min((int)threadIdx.x, MM - 1)];
+        stage_acts<MM>(act, xq, K, 0, cols0, [&]() __attribute__((always_inline)) { issue(bA, 0); });
+        // scales in LDS: a lane-dependent index into a register array would put it in scratch memory
+        if (threadIdx.x < MM) xs_w[threadIdx.x] = xsv;
+        float cb[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) cb[c] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(codebook[c])));
+        build_level_table_regs(lut, cb, threadIdx.x, GV_THREADS);
+    }
     __syncthreads();
 
-    const float* xs_lds = reinterpret_cast<const float*>(act + MM * SLAB);   // staged below
+    const float* xs_lds = xs_w;
     int32_t acc[R * MM];
     int slab_k0 = 0;
 
@@ -258,8 +399,8 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
         }
     };
     if (nsteps == 1) body(0, bA, bB, true, std::true_type{}, std::false_type{});   // one tile, one batch
-    else if (K <= SLAB) run(std::true_type{});
-    else run(std::false_type{});
+    else if (FUSED || K <= SLAB) run(std::true_type{});
+    else if constexpr (!FUSED) run(std::false_type{});
 }
 
 template <int MM, int R>
@@ -271,6 +412,20 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(const int8_t* __restri
                                                           const float* __restrict__ bias, int N, int K,
                                                           int out_type, void* __restrict__ out) {
     gemv_body<MM, R>(xq, xs, qp, srel, codebook, ws, bias, N, K, out_type, out, blockIdx.x, 1);
+}
+
+template <int MM, int R, bool LONGK>
+__global__ __launch_bounds__(GV_THREADS) void gemv_act_kernel(const uint16_t* __restrict__ x, int qmax,
+                                                              const uint8_t* __restrict__ qp,
+                                                              const uint8_t* __restrict__ srel,
+                                                              const float* __restrict__ codebook,
+                                                              const float* __restrict__ ws,
+                                                              const float* __restrict__ bias, int N, int K,
+                                                              int out_type, void* __restrict__ out,
+                                                              int8_t* __restrict__ xq_out, float* __restrict__ xs_out) {
+    const bool first = blockIdx.x == 0;   // one block writes the prepared activations out
+    gemv_body<MM, R, true, LONGK>(nullptr, nullptr, qp, srel, codebook, ws, bias, N, K, out_type, out, blockIdx.x, 1, x,
+                           qmax, first ? xq_out : nullptr, first ? xs_out : nullptr);
 }
 
 // Several independent layers (same M) in one launch: block b works on the layer whose
@@ -322,7 +477,7 @@ hipError_t launch_gemv_grouped_m(const w4a8_gemv_layer* layers, int count, int o
             a.first[i + 1] = a.first[i] + (tiles + tpb - 1) / tpb;
         }
         for (int i = a.count; i < GEMV_GROUP_MAX; ++i) a.first[i + 1] = a.first[a.count];
-        const size_t lds = 4096 + (size_t)MM * slab_cols(MM) + 32;
+        const size_t lds = gemv_lds_bytes(MM, false);
         const dim3 g(a.first[a.count]), b(GV_THREADS);
         if (R == 2)
             hipLaunchKernelGGL((gemv_grouped_kernel<MM, 2>), g, b, lds, stream, a, out_type);
@@ -341,7 +496,7 @@ hipError_t launch_gemv_m(const int8_t* xq, const float* xs, const uint8_t* qp, c
     const int waves_per_block = GV_THREADS / 64;
     const int R = rows_per_wave(N);
     const int blocks = (N + waves_per_block * R - 1) / (waves_per_block * R);
-    const size_t lds = 4096 + (size_t)MM * slab_cols(MM) + 32;
+    const size_t lds = gemv_lds_bytes(MM, false);
     const dim3 g(blocks), b(GV_THREADS);
     if (R == 2)
         hipLaunchKernelGGL((gemv_kernel<MM, 2>), g, b, lds, stream, xq, xs, qp, srel, codebook, ws, bias, N, K,
@@ -352,7 +507,48 @@ hipError_t launch_gemv_m(const int8_t* xq, const float* xs, const uint8_t* qp, c
     return hipGetLastError();
 }
 
+template <int MM>
+hipError_t launch_gemv_act_m(const uint16_t* x, int qmax, const uint8_t* qp, const uint8_t* srel,
+                             const float* codebook, const float* ws, const float* bias, int N, int K, int out_type,
+                             void* out, int8_t* xq_out, float* xs_out, hipStream_t stream) {
+    const int waves_per_block = GV_THREADS / 64;
+    const int R = rows_per_wave(N);
+    const int blocks = (N + waves_per_block * R - 1) / (waves_per_block * R);
+    const size_t lds = gemv_lds_bytes(MM, true);
+    const dim3 g(blocks), b(GV_THREADS);
+#define GV_ACT_LAUNCH(RR, LL)                                                                               \
+    hipLaunchKernelGGL((gemv_act_kernel<MM, RR, LL>), g, b, lds, stream, x, qmax, qp, srel, codebook, ws, bias, N, \
+                       K, out_type, out, xq_out, xs_out)
+    if constexpr (slab_cols(MM) > 4096) {
+        if (K > 4096) {
+            if (R == 2) GV_ACT_LAUNCH(2, true);
+            else GV_ACT_LAUNCH(1, true);
+            return hipGetLastError();
+        }
+    }
+    if (R == 2) GV_ACT_LAUNCH(2, false);
+    else GV_ACT_LAUNCH(1, false);
+#undef GV_ACT_LAUNCH
+    return hipGetLastError();
+}
+
 }  // namespace
+
+int gemv_act_max_k(int M) { return M >= 1 && M <= 8 ? slab_cols(M) : 0; }
+
+hipError_t launch_gemv_act(const uint16_t* x, int M, int qmax, const uint8_t* qp, const uint8_t* srel,
+                           const float* codebook, const float* ws, const float* bias, int N, int K, int out_type,
+                           void* out, int8_t* xq_out, float* xs_out, hipStream_t stream) {
+    (void)hipGetLastError();   // clear a stale error so the check below is about this launch
+    switch (M) {
+#define GV_ACT_CASE(MMV) \
+        case MMV: return launch_gemv_act_m<MMV>(x, qmax, qp, srel, codebook, ws, bias, N, K, out_type, out, xq_out, xs_out, stream);
+        GV_ACT_CASE(1) GV_ACT_CASE(2) GV_ACT_CASE(3) GV_ACT_CASE(4)
+        GV_ACT_CASE(5) GV_ACT_CASE(6) GV_ACT_CASE(7) GV_ACT_CASE(8)
+#undef GV_ACT_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_gemv_grouped(const w4a8_gemv_layer* layers, int count, int M, int out_type, hipStream_t stream) {
     (void)hipGetLastError();   // clear a stale error so the checks below are about these launches

@@ -30,86 +30,12 @@
 // keep up to CH passes of rotated values in registers between the absmax and the
 // quantisation, or recompute them (CH == 0) for very long rows.
 #include "w4a8_device.hpp"
+#include "rotq_device.hpp"
 
 namespace w4a8 {
 namespace {
 
 constexpr int RQ_THREADS = 256;
-constexpr int TSTRIDE = 17;   // padded row of the fp64 transpose buffer (bank spread)
-
-__device__ __forceinline__ void radix4(double& a0, double& a1, double& a2, double& a3) {
-    const double s = (a0 + a1) + (a2 + a3);
-    const double b0 = __builtin_fma(-2.0, a3, s), b1 = __builtin_fma(-2.0, a2, s);
-    const double b2 = __builtin_fma(-2.0, a1, s), b3 = __builtin_fma(-2.0, a0, s);
-    a0 = b0; a1 = b1; a2 = b2; a3 = b3;
-}
-
-// radix-16 over v[4*d1 + d0]: the stage of digit d0, then of digit d1
-__device__ __forceinline__ void radix16(double (&v)[16]) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) radix4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) radix4(v[g], v[g + 4], v[g + 8], v[g + 12]);
-}
-
-// Rotate block `blk` of row `row`.  Every thread of the block must call this (it
-// synchronises); threads with ok == false contribute zeros.  On return r[i] holds
-// the rotated value of column 16*i + l16 of the block, rounded to fp32.
-__device__ __forceinline__ void rotate_block(const uint16_t* __restrict__ x, int64_t row, int K, int blk,
-                                             bool ok, int slot, int l16, double* tbuf, float (&r)[16]) {
-    double v[16];
-    if (ok) {
-        const uint4* src = reinterpret_cast<const uint4*>(x + row * K + (int64_t)blk * 256 + l16 * 16);
-        const uint4 p0 = src[0], p1 = src[1];
-        const uint32_t w[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            v[2 * i] = (double)__uint_as_float(w[i] << 16);
-            v[2 * i + 1] = (double)__uint_as_float(w[i] & 0xFFFF0000u);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = 0.0;
-    }
-    radix16(v);     // digits 0, 1 of the input column (inside the lane)
-    double* t = tbuf + slot * (16 * TSTRIDE);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) t[l16 * TSTRIDE + i] = v[i];
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = t[j * TSTRIDE + l16];
-    __syncthreads();
-    radix16(v);     // digits 2, 3 (the lane index of the first half)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) r[i] = (float)(v[i] * 0.0625);
-}
-
-__device__ __forceinline__ float slot_max(float a) {
-    a = __builtin_fmaxf(a, __shfl_xor(a, 8, 16));
-    a = __builtin_fmaxf(a, __shfl_xor(a, 4, 16));
-    a = __builtin_fmaxf(a, __shfl_xor(a, 2, 16));
-    a = __builtin_fmaxf(a, __shfl_xor(a, 1, 16));
-    return a;
-}
-
-__device__ __forceinline__ int8_t quant1(float v, double inv, float qmaxf) {
-    float q = __builtin_rintf((float)((double)v * inv));
-    q = __builtin_fminf(__builtin_fmaxf(q, -qmaxf), qmaxf);
-    return (int8_t)(int32_t)q;
-}
-
-// Quantise one rotated block held as r[i] = column 16*i + l16 and store it.
-__device__ __forceinline__ void quant_store(const float (&r)[16], double inv, float qmaxf, bool ok,
-                                            int8_t* __restrict__ xq, int64_t row, int K, int blk,
-                                            int slot, int l16, uint8_t* qbuf) {
-    uint8_t* qb = qbuf + slot * 256;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) qb[16 * i + l16] = (uint8_t)quant1(r[i], inv, qmaxf);
-    __syncthreads();
-    const uint4 out = *reinterpret_cast<const uint4*>(qb + 16 * l16);
-    if (ok) *reinterpret_cast<uint4*>(xq + row * K + (int64_t)blk * 256 + 16 * l16) = out;
-    __syncthreads();
-}
 
 template <int CH>
 __global__ __launch_bounds__(RQ_THREADS) void rotate_quant_kernel(const uint16_t* __restrict__ x, int64_t M, int K,

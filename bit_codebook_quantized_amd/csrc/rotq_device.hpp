@@ -1,0 +1,115 @@
+// Device helpers of the activation rotation and quantisation, shared by
+// rotate_quant_act and the GEMV that takes bf16 activations, so both compute the
+// same values bit for bit.
+//
+// Rotation (h3-rs 0.2.0 src/weights.rs, fn hadamard / fn rotate_activation): each
+// 256-column block of a row is multiplied by H4^(x4) / 16.  H4 = J - 2R (all-ones
+// minus twice the reversal), so a radix-4 stage maps (a0..a3) to
+// out_i = (a0 + a1 + a2 + a3) - 2 a_(3-i).  The stages run in fp64 on bf16 inputs,
+// where the partial sums are exact, and the result is rounded once to fp32.
+//
+// Quantisation (ai-toolkit convrot_w4a8_quant.py, w4a8_act_quant_kernel):
+// q = round_half_even(fp32(v / scale)) clamped to [-qmax, qmax], with fp32(v / scale)
+// computed as fp32(v * fp64(1 / scale)) (the fp64 product is within 2^-52 of the
+// quotient, which is never closer than 2^-49 to an fp32 rounding midpoint).
+//
+// A rotation slot is 16 lanes; 16 slots (256 threads) share a transpose buffer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a8 {
+
+constexpr int TSTRIDE = 17;   // padded row of the fp64 transpose buffer (bank spread)
+constexpr int ROTQ_TBUF_DOUBLES = 16 * 16 * TSTRIDE;   // one 16 x 16 tile per slot
+
+__device__ __forceinline__ void radix4(double& a0, double& a1, double& a2, double& a3) {
+    const double s = (a0 + a1) + (a2 + a3);
+    const double b0 = __builtin_fma(-2.0, a3, s), b1 = __builtin_fma(-2.0, a2, s);
+    const double b2 = __builtin_fma(-2.0, a1, s), b3 = __builtin_fma(-2.0, a0, s);
+    a0 = b0; a1 = b1; a2 = b2; a3 = b3;
+}
+
+// radix-16 over v[4*d1 + d0]: the stage of digit d0, then of digit d1
+__device__ __forceinline__ void radix16(double (&v)[16]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) radix4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) radix4(v[g], v[g + 4], v[g + 8], v[g + 12]);
+}
+
+// The 16 bf16 inputs of a lane: columns 16*l16 .. 16*l16 + 15 of block `blk` of row
+// `row` (two 16-byte loads).
+struct RotIn {
+    uint4 p0, p1;
+};
+
+__device__ __forceinline__ RotIn rot_load(const uint16_t* __restrict__ x, int64_t row, int K, int blk, int l16) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + row * K + (int64_t)blk * 256 + l16 * 16);
+    return RotIn{src[0], src[1]};
+}
+
+// Rotate one block from its loaded inputs.  Every thread of the block must call this
+// (it synchronises); threads with ok == false contribute zeros.  On return r[i] holds
+// the rotated value of column 16*i + l16 of the block, rounded to fp32.
+__device__ __forceinline__ void rotate_loaded(const RotIn in, bool ok, int slot, int l16, double* tbuf,
+                                              float (&r)[16]) {
+    double v[16];
+    const uint32_t w[8] = {in.p0.x, in.p0.y, in.p0.z, in.p0.w, in.p1.x, in.p1.y, in.p1.z, in.p1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t wi = ok ? w[i] : 0u;
+        v[2 * i] = (double)__uint_as_float(wi << 16);
+        v[2 * i + 1] = (double)__uint_as_float(wi & 0xFFFF0000u);
+    }
+    radix16(v);     // digits 0, 1 of the input column (inside the lane)
+    double* t = tbuf + slot * (16 * TSTRIDE);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t[l16 * TSTRIDE + i] = v[i];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = t[j * TSTRIDE + l16];
+    __syncthreads();
+    radix16(v);     // digits 2, 3 (the lane index of the first half)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = (float)(v[i] * 0.0625);
+}
+
+// Load and rotate block `blk` of row `row` (see rotate_loaded).
+__device__ __forceinline__ void rotate_block(const uint16_t* __restrict__ x, int64_t row, int K, int blk,
+                                             bool ok, int slot, int l16, double* tbuf, float (&r)[16]) {
+    RotIn in{};
+    if (ok) in = rot_load(x, row, K, blk, l16);
+    rotate_loaded(in, ok, slot, l16, tbuf, r);
+}
+
+__device__ __forceinline__ float slot_max(float a) {
+    a = __builtin_fmaxf(a, __shfl_xor(a, 8, 16));
+    a = __builtin_fmaxf(a, __shfl_xor(a, 4, 16));
+    a = __builtin_fmaxf(a, __shfl_xor(a, 2, 16));
+    a = __builtin_fmaxf(a, __shfl_xor(a, 1, 16));
+    return a;
+}
+
+__device__ __forceinline__ int8_t quant1(float v, double inv, float qmaxf) {
+    float q = __builtin_rintf((float)((double)v * inv));
+    q = __builtin_fminf(__builtin_fmaxf(q, -qmaxf), qmaxf);
+    return (int8_t)(int32_t)q;
+}
+
+// Quantise one rotated block held as r[i] = column 16*i + l16 and store it.
+__device__ __forceinline__ void quant_store(const float (&r)[16], double inv, float qmaxf, bool ok,
+                                            int8_t* __restrict__ xq, int64_t row, int K, int blk,
+                                            int slot, int l16, uint8_t* qbuf) {
+    uint8_t* qb = qbuf + slot * 256;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) qb[16 * i + l16] = (uint8_t)quant1(r[i], inv, qmaxf);
+    __syncthreads();
+    const uint4 out = *reinterpret_cast<const uint4*>(qb + 16 * l16);
+    if (ok) *reinterpret_cast<uint4*>(xq + row * K + (int64_t)blk * 256 + 16 * l16) = out;
+    __syncthreads();
+}
+
+
+}  // namespace w4a8

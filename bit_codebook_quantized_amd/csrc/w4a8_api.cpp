@@ -20,6 +20,10 @@ hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, const uint8_t* 
                        const float* codebook, const float* ws, const float* bias, int N, int K, int out_type,
                        void* out, hipStream_t stream);
 hipError_t launch_gemv_grouped(const w4a8_gemv_layer* layers, int count, int M, int out_type, hipStream_t stream);
+hipError_t launch_gemv_act(const uint16_t* x, int M, int qmax, const uint8_t* qp, const uint8_t* srel,
+                           const float* codebook, const float* ws, const float* bias, int N, int K, int out_type,
+                           void* out, int8_t* xq_out, float* xs_out, hipStream_t stream);
+int gemv_act_max_k(int M);
 hipError_t launch_quantize(const float* w, int64_t N, int K, int rotated, const float* codebook, uint8_t* qpacked,
                            uint8_t* srel, float* s_channel, hipStream_t stream);
 }  // namespace w4a8
@@ -117,6 +121,34 @@ int w4a8_gemv(const int8_t* xq, const float* xs, int64_t M, const uint8_t* qpack
                                       out_type, out, static_cast<hipStream_t>(stream)));
 }
 
+int w4a8_gemv_act(const void* x, int64_t M, int32_t rot_block, int32_t qmax, const uint8_t* qpacked,
+                  const uint8_t* srel, const float* codebook, const float* s_channel, const float* bias, int64_t N,
+                  int64_t K, int32_t group, int32_t out_type, void* out, int8_t* xq_out, float* xs_out,
+                  void* stream) {
+    if (M < 0) return W4A8_ERR_INVALID_ARG;
+    int st = check_n(N);
+    if (st) return st;
+    if ((st = check_k(K))) return st;
+    if (out_type < W4A8_OUT_BF16 || out_type > W4A8_OUT_I32) return W4A8_ERR_INVALID_ARG;
+    if (group != W4A8_GROUP || rot_block != W4A8_ROT_BLOCK || qmax < 1 || qmax > 127) return W4A8_ERR_UNSUPPORTED;
+    if (M > W4A8_GEMV_MAX_M) return W4A8_ERR_UNSUPPORTED;
+    if (!qpacked || !srel || !codebook || !s_channel) return W4A8_ERR_INVALID_ARG;
+    if ((xq_out == nullptr) != (xs_out == nullptr)) return W4A8_ERR_INVALID_ARG;
+    if (M > 0 && (!x || !out)) return W4A8_ERR_INVALID_ARG;
+    if (!aligned(qpacked, 16) || !aligned(srel, 16) || !aligned(codebook, 4) || !aligned(s_channel, 4) ||
+        !aligned(bias, 4))
+        return W4A8_ERR_ALIGN;
+    if (M > 0 && (!aligned(x, 16) || !aligned(out, 16) || !aligned(xq_out, 16) || !aligned(xs_out, 4)))
+        return W4A8_ERR_ALIGN;
+    if (M == 0) return W4A8_OK;
+    if (K > w4a8::gemv_act_max_k((int)M)) return W4A8_ERR_UNSUPPORTED;
+    return launched(w4a8::launch_gemv_act(static_cast<const uint16_t*>(x), (int)M, qmax, qpacked, srel, codebook,
+                                          s_channel, bias, (int)N, (int)K, out_type, out, xq_out, xs_out,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int64_t w4a8_gemv_act_max_k(int64_t M) { return M >= 1 && M <= W4A8_GEMV_MAX_M ? w4a8::gemv_act_max_k((int)M) : 0; }
+
 int w4a8_gemv_grouped(const w4a8_gemv_layer* layers, int32_t count, int64_t M, int32_t group, int32_t out_type,
                       void* stream) {
     if (count < 0 || M < 0) return W4A8_ERR_INVALID_ARG;
@@ -161,6 +193,6 @@ const char* w4a8_status_string(int status) {
     }
 }
 
-int w4a8_abi_version(void) { return 3; }
+int w4a8_abi_version(void) { return 4; }
 
 }  // extern "C"

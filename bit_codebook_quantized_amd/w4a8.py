@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so"
 OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP = range(6)
 OUT_BF16, OUT_F32, OUT_I32 = 0, 1, 2
 ROT_BLOCK, GROUP, GEMV_MAX_M, MAX_K = 256, 16, 8, 131072
-ABI_VERSION = 3
+ABI_VERSION = 4
+FUSED_ACT_MAX_K = 4096   # linear() uses w4a8_gemv_act for one row up to this K
 _OUT_CODES = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32, torch.int32: OUT_I32}
 
 # The default 16-level table (ai-toolkit convrot_w4a8_quant.py, FIXED_CODEBOOK):
@@ -44,6 +45,8 @@ SIGNATURES = {
     "w4a8_gemv": [_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P],
     "quantize_w4": [_P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P],
     "w4a8_gemv_grouped": [_P, _I32, _I64, _I32, _I32, _P],
+    "w4a8_gemv_act": [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _P, _P],
+    "w4a8_gemv_act_max_k": [_I64],
     "w4a8_status_string": [ctypes.c_int],
     "w4a8_abi_version": [],
 }
@@ -78,7 +81,8 @@ def load() -> ctypes.CDLL:
         for name, args in SIGNATURES.items():
             fn = getattr(lib, name)
             fn.argtypes = args
-            fn.restype = ctypes.c_char_p if name == "w4a8_status_string" else ctypes.c_int
+            fn.restype = {"w4a8_status_string": ctypes.c_char_p, "w4a8_gemv_act_max_k": ctypes.c_int64}.get(
+                name, ctypes.c_int)
         if lib.w4a8_abi_version() != ABI_VERSION:
             raise ImportError("libw4a8.so ABI version mismatch")
         _lib = lib
@@ -215,6 +219,40 @@ def w4a8_gemv(xq, xs, layer: W4A8Layer, out_dtype=torch.bfloat16, out=None):
     return _linear_call("w4a8_gemv", xq, xs, layer, out_dtype, out)
 
 
+def gemv_act_max_k(m: int) -> int:
+    """Largest K that w4a8_gemv_act takes for m rows (0 outside 1..8)."""
+    return int(load().w4a8_gemv_act_max_k(int(m)))
+
+
+def w4a8_gemv_act(x: torch.Tensor, layer: W4A8Layer, out_dtype=torch.bfloat16, out=None, qmax: int = 127,
+                  xq_out: torch.Tensor = None, xs_out: torch.Tensor = None):
+    """The whole layer for bf16 x [M, K], M <= 8, in one launch (rotation and
+    quantisation done inside the GEMV).  Bit-identical to rotate_quant_act followed by
+    w4a8_gemv.  xq_out / xs_out (both or neither) receive the prepared activations."""
+    layer.check()
+    _dev(x, torch.bfloat16, "x")
+    m, k = x.shape
+    n = layer.out_features
+    if k != layer.in_features:
+        raise ValueError(f"x has K={k}, layer has K={layer.in_features}")
+    if out_dtype not in _OUT_CODES:
+        raise ValueError(f"unsupported out_dtype {out_dtype}")
+    if (xq_out is None) != (xs_out is None):
+        raise ValueError("xq_out and xs_out go together")
+    out = _out(out, (m, n), out_dtype, x.device, "out")
+    if xq_out is not None:
+        _out(xq_out, (m, k), torch.int8, x.device, "xq_out")
+        _out(xs_out, (m,), torch.float32, x.device, "xs_out")
+    bias = layer.bias.data_ptr() if layer.bias is not None else None
+    st = load().w4a8_gemv_act(x.data_ptr(), m, ROT_BLOCK, qmax, layer.qpacked.data_ptr(), layer.srel.data_ptr(),
+                              layer.codebook.data_ptr(), layer.s_channel.data_ptr(), bias, n, k, GROUP,
+                              _OUT_CODES[out_dtype], out.data_ptr(),
+                              None if xq_out is None else xq_out.data_ptr(),
+                              None if xs_out is None else xs_out.data_ptr(), _stream(x))
+    _check("w4a8_gemv_act", st)
+    return out
+
+
 def _group_descs(items, out_dtype):
     """items: (xq, xs, layer, out or None) per layer, common M -> (ctypes array, outs, M)."""
     if out_dtype not in _OUT_CODES:
@@ -285,9 +323,13 @@ def quantize_w4(w: torch.Tensor, codebook=None, rotated: bool = False, bias=None
 
 def linear(x: torch.Tensor, layer: W4A8Layer, out_dtype=torch.bfloat16) -> torch.Tensor:
     """The whole layer for bf16 x [..., K]: rotate + quantise, then the GEMV for at
-    most 8 rows and the GEMM otherwise."""
+    most 8 rows and the GEMM otherwise; a single row with K <= FUSED_ACT_MAX_K takes
+    the one-launch w4a8_gemv_act instead (measured faster there only: every workgroup
+    repeats the rotation, which costs more than the saved launch for more rows)."""
     shape = x.shape
     x2 = x.reshape(-1, shape[-1]).contiguous()
+    if x2.shape[0] == 1 and x2.shape[1] <= FUSED_ACT_MAX_K:
+        return w4a8_gemv_act(x2, layer, out_dtype).reshape(*shape[:-1], layer.out_features)
     xq, xs = rotate_quant_act(x2)
     fn = w4a8_gemv if x2.shape[0] <= GEMV_MAX_M else w4a8_gemm
     y = fn(xq, xs, layer, out_dtype)
@@ -317,6 +359,15 @@ def prepared_linear(fn: str, xq, xs, layer: W4A8Layer, out):
     bias = layer.bias.data_ptr() if layer.bias is not None else None
     return prepare(fn, xq, xs, xq.shape[0], layer.qpacked, layer.srel, layer.codebook, layer.s_channel, bias,
                    layer.out_features, layer.in_features, GROUP, _OUT_CODES[out.dtype], out)
+
+
+def prepared_gemv_act(x, layer: W4A8Layer, out, qmax: int = 127):
+    """prepare() for w4a8_gemv_act (no prepared-activation outputs)."""
+    w4a8_gemv_act(x, layer, out.dtype, out, qmax)           # validates shapes and runs once
+    bias = layer.bias.data_ptr() if layer.bias is not None else None
+    return prepare("w4a8_gemv_act", x, x.shape[0], ROT_BLOCK, qmax, layer.qpacked, layer.srel, layer.codebook,
+                   layer.s_channel, bias, layer.out_features, layer.in_features, GROUP, _OUT_CODES[out.dtype], out,
+                   None, None)
 
 
 def prepared_rotate_quant(x, xq, xs, qmax: int = 127):

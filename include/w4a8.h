@@ -52,7 +52,8 @@ enum w4a8_status {
     W4A8_ERR_SHAPE = 2,        /* N < 1, K not a positive multiple of 256, K > W4A8_MAX_K */
     W4A8_ERR_ALIGN = 3,        /* a pointer misses its required alignment */
     W4A8_ERR_UNSUPPORTED = 4,  /* group != 16, rot_block != 256, qmax not in 1..127,
-                                  M > W4A8_GEMV_MAX_M for w4a8_gemv */
+                                  M > W4A8_GEMV_MAX_M for the GEMV entry points,
+                                  K > w4a8_gemv_act_max_k(M) for w4a8_gemv_act */
     W4A8_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
 };
 
@@ -131,6 +132,37 @@ int w4a8_gemv(const int8_t* xq, const float* xs, int64_t M,
               const uint8_t* qpacked, const uint8_t* srel, const float* codebook,
               const float* s_channel, const float* bias, int64_t N, int64_t K, int32_t group,
               int32_t out_type, void* out, void* stream);
+
+/*
+ * w4a8_gemv_act -- steps 1 to 5 in one launch for 1 <= M <= W4A8_GEMV_MAX_M: the decode
+ * GEMV taking the bf16 activation rows themselves.  Every workgroup rotates and
+ * quantises the M rows in on-chip memory with the arithmetic of rotate_quant_act
+ * (ai-toolkit ConvRotW4A8Quantizer.forward on the decode path: prepare_act, then the
+ * GEMV), so the result is bit-identical to rotate_quant_act followed by w4a8_gemv.
+ *
+ *   x                   in   bf16 bits [M, K]
+ *   M                        rows, 0..W4A8_GEMV_MAX_M
+ *   rot_block, qmax          as for rotate_quant_act
+ *   qpacked, srel,      in   the layer storage
+ *   codebook, s_channel
+ *   bias                in   float [N] or NULL
+ *   N, K, group, out_type    as for w4a8_gemm
+ *   out                 out  [M, N] of the chosen type
+ *   xq_out, xs_out      out  NULL, or int8 [M, K] and float [M]: the quantised rows and
+ *                            their scales, as rotate_quant_act would write them (for a
+ *                            caller that shares them with other layers); both or neither
+ *
+ * K must not exceed w4a8_gemv_act_max_k(M) (the rows are held on chip); larger K, or
+ * M > W4A8_GEMV_MAX_M, returns W4A8_ERR_UNSUPPORTED.
+ */
+int w4a8_gemv_act(const void* x, int64_t M, int32_t rot_block, int32_t qmax,
+                  const uint8_t* qpacked, const uint8_t* srel, const float* codebook,
+                  const float* s_channel, const float* bias, int64_t N, int64_t K, int32_t group,
+                  int32_t out_type, void* out, int8_t* xq_out, float* xs_out, void* stream);
+
+/* Largest K that w4a8_gemv_act accepts for M rows (32768 / 16384 / 8192 / 4096 for
+ * M = 1 / 2 / 3..4 / 5..8); 0 for M outside 1..W4A8_GEMV_MAX_M. */
+int64_t w4a8_gemv_act_max_k(int64_t M);
 
 /*
  * w4a8_gemv_grouped -- w4a8_gemv for several independent layers in as few launches as

@@ -28,9 +28,9 @@ def w4a8():
 def test_header_declares_the_operations():
     names = _declared_functions()
     for n in ("rotate_quant_act", "decode_w4_to_int8", "w4a8_gemm", "w4a8_gemv", "w4a8_gemv_grouped",
-              "quantize_w4", "w4a8_status_string", "w4a8_abi_version"):
+              "quantize_w4", "w4a8_gemv_act", "w4a8_gemv_act_max_k", "w4a8_status_string", "w4a8_abi_version"):
         assert n in names
-    assert len(names) == 8, names
+    assert len(names) == 10, names
 
 
 def test_library_exports_every_declared_symbol(w4a8):
@@ -45,7 +45,7 @@ def test_status_strings(w4a8):
         "W4A8_OK", "W4A8_ERR_INVALID_ARG", "W4A8_ERR_SHAPE", "W4A8_ERR_ALIGN", "W4A8_ERR_UNSUPPORTED",
         "W4A8_ERR_HIP"]
     assert w4a8.status_string(99) == "W4A8_ERR_UNKNOWN"
-    assert w4a8.load().w4a8_abi_version() == w4a8.ABI_VERSION == 3
+    assert w4a8.load().w4a8_abi_version() == w4a8.ABI_VERSION == 4
 
 
 A = 1 << 20          # a 16-byte-aligned fake address (never dereferenced: validation fails first)
@@ -85,6 +85,39 @@ def test_gemv_rejects_more_than_8_rows(w4a8):
     assert _lin(w4a8, "w4a8_gemv", M=9, qp=U) == w4a8.ERR_ALIGN      # validation order: storage first
     assert _lin(w4a8, "w4a8_gemv", M=9, K=100) == w4a8.ERR_SHAPE
     assert _lin(w4a8, "w4a8_gemv", M=9, group=8) == w4a8.ERR_UNSUPPORTED
+
+
+def _act(w4a8, **kw):
+    a = dict(x=A, M=4, rot=256, qmax=127, qp=A, srel=A, cb=A, sch=A, bias=None, N=64, K=256, group=16, out_type=0,
+             out=A, xq_out=None, xs_out=None)
+    a.update(kw)
+    return w4a8.call("w4a8_gemv_act", a["x"], a["M"], a["rot"], a["qmax"], a["qp"], a["srel"], a["cb"], a["sch"],
+                     a["bias"], a["N"], a["K"], a["group"], a["out_type"], a["out"], a["xq_out"], a["xs_out"], None)
+
+
+def test_gemv_act_validation(w4a8):
+    assert [w4a8.gemv_act_max_k(m) for m in range(10)] == [0, 32768, 16384, 8192, 8192, 4096, 4096, 4096, 4096, 0]
+    assert _act(w4a8, M=-1) == w4a8.ERR_INVALID_ARG
+    assert _act(w4a8, M=9) == w4a8.ERR_UNSUPPORTED
+    assert _act(w4a8, M=5, K=4096 + 256) == w4a8.ERR_UNSUPPORTED     # rows do not fit on chip
+    assert _act(w4a8, M=1, K=32768 + 256) == w4a8.ERR_UNSUPPORTED
+    assert _act(w4a8, N=0) == w4a8.ERR_SHAPE
+    assert _act(w4a8, K=300) == w4a8.ERR_SHAPE
+    assert _act(w4a8, rot=128) == w4a8.ERR_UNSUPPORTED
+    assert _act(w4a8, qmax=0) == w4a8.ERR_UNSUPPORTED
+    assert _act(w4a8, qmax=128) == w4a8.ERR_UNSUPPORTED
+    assert _act(w4a8, group=32) == w4a8.ERR_UNSUPPORTED
+    assert _act(w4a8, out_type=3) == w4a8.ERR_INVALID_ARG
+    for p in ("x", "out", "qp", "srel", "cb", "sch"):
+        assert _act(w4a8, **{p: None}) == w4a8.ERR_INVALID_ARG, p
+    assert _act(w4a8, xq_out=A) == w4a8.ERR_INVALID_ARG                # one of the pair
+    assert _act(w4a8, xs_out=A) == w4a8.ERR_INVALID_ARG
+    for p in ("x", "out", "qp", "srel", "xq_out"):
+        kw = {"xq_out": A, "xs_out": A}
+        kw[p] = A + 8
+        assert _act(w4a8, **kw) == w4a8.ERR_ALIGN, p
+    assert _act(w4a8, xq_out=A, xs_out=A + 2) == w4a8.ERR_ALIGN
+    assert _act(w4a8, M=0, x=None, out=None, qp=U) == w4a8.ERR_ALIGN
 
 
 def test_rotate_quant_validation(w4a8):
