@@ -43,6 +43,9 @@ __all__ = [
     "rotate_quant_act", "pack_codes", "unpack_codes", "decode_w4",
     "assign_codes", "grid_levels", "assign_grid", "quantize_w4_rotated",
     "quantize_w4", "gemm_exact", "epilogue", "linear", "dequantize",
+    "assign_grid_stochastic", "requantize_codes", "fake_quant_rotated", "dequantize_f32",
+    "ste_weight_bf16", "grad_input_exact", "interleave_rows", "swiglu_interleaved", "lora_delta",
+    "lora_merge_weight",
 ]
 
 F32 = np.float32
@@ -402,3 +405,136 @@ def dequantize(packed, srel_u8, s_channel, codebook, block: int = ROT_BLOCK, gro
     w8 = decode_w4(packed, srel_u8, codebook, group).astype(np.float64)
     w_rot = w8 * np.asarray(s_channel, dtype=np.float64)[:, None]
     return rotate(w_rot, block)
+
+
+# ----------------------------------------------------------------------------
+# training path  ([AT] _assign_grid stochastic branch, requantize_codes_,
+# fake_quant_rotated_weight, _w4a8_linear_ste_backward, dequantize_w4a8)
+
+def assign_grid_stochastic(target, levels, u) -> np.ndarray:
+    """[AT] _assign_grid with stochastic=True: the bracket below each target is
+    found from its left insertion point p among the 16 non-decreasing levels (the
+    count of levels below it), lo = clamp(p - 1, 0, 14); the threshold
+    thr = u * (lv[lo + 1] - lv[lo]) + lv[lo] (fp32, the product rounded, then the
+    sum rounded); the code is lo + 1 when target > thr, else lo.  u [N, G, g] are
+    the uniform draws in [0, 1) (inputs: the page draws them with rand_like)."""
+    t = np.asarray(target, dtype=F32)
+    lv = np.asarray(levels, dtype=F32)
+    uu = np.asarray(u, dtype=F32)
+    last = lv.shape[-1] - 1
+    pos = (lv[:, :, None, :] < t[:, :, :, None]).sum(axis=-1)
+    lo = np.clip(pos - 1, 0, last - 1)
+    lv_lo = np.take_along_axis(lv, lo.reshape(lv.shape[0], lv.shape[1], -1), axis=2).reshape(t.shape)
+    lv_hi = np.take_along_axis(lv, (lo + 1).reshape(lv.shape[0], lv.shape[1], -1), axis=2).reshape(t.shape)
+    width = (lv_hi - lv_lo).astype(F32)
+    thr = ((uu * width).astype(F32) + lv_lo).astype(F32)
+    return np.clip(lo + (t > thr), 0, last)
+
+
+def requantize_codes(w, srel_u8, s_channel, codebook, rotated: bool = False, u=None,
+                     block: int = ROT_BLOCK, group: int = GROUP) -> np.ndarray:
+    """[AT] ConvRotW4A8Quantizer.requantize_codes_: new codes for the fp32 weight
+    w [N, K] on the layer's stored group scales, channel scales and codebook (the
+    grid a quantisation-aware run trains against).  The weight is rotated (exact,
+    rounded once to fp32) unless ``rotated``; target = w_rot / s_channel in fp32;
+    codes = nearest grid level ([AT] _assign_grid), or the unbiased stochastic
+    choice between the bracketing levels when the uniform draws ``u`` [N, K] are
+    given.  Returns the packed codes u8 [N, K/2]."""
+    w = np.asarray(w, dtype=F32)
+    n, k = w.shape
+    w_rot = w if rotated else rotate_to_f32(w, block)
+    target = (w_rot.reshape(n, k // group, group) / np.asarray(s_channel, dtype=F32)[:, None, None]).astype(F32)
+    levels = grid_levels(codebook, srel_u8)
+    if u is None:
+        codes = assign_grid(target, levels)
+    else:
+        codes = assign_grid_stochastic(target, levels, np.asarray(u, dtype=F32).reshape(target.shape))
+    return pack_codes(codes.reshape(n, k))
+
+
+def fake_quant_rotated(w_rot, srel_u8, s_channel, codebook, group: int = GROUP) -> np.ndarray:
+    """[AT] ConvRotW4A8Quantizer.fake_quant_rotated_weight: dequant(quant(w_rot))
+    on the stored scales: the nearest grid level of w_rot / s_channel (as in
+    requantize_codes) times s_channel, in fp32.  Returns fp32 [N, K]."""
+    w_rot = np.asarray(w_rot, dtype=F32)
+    n, k = w_rot.shape
+    sch = np.asarray(s_channel, dtype=F32)
+    target = (w_rot.reshape(n, k // group, group) / sch[:, None, None]).astype(F32)
+    levels = grid_levels(codebook, srel_u8)
+    codes = assign_grid(target, levels)
+    lv = np.take_along_axis(levels, codes, axis=2)
+    return (lv.reshape(n, k) * sch[:, None]).astype(F32)
+
+
+def dequantize_f32(packed, srel_u8, s_channel, codebook, rotate_back: bool = True,
+                   block: int = ROT_BLOCK, group: int = GROUP) -> np.ndarray:
+    """[AT] dequantize_w4a8 in fp32: w8 * s_channel (fp32 product), then rotated
+    back to the original basis (exact block product rounded once to fp32: the
+    256 terms of a block share the row scale, so the fp64 sum is exact).  With
+    ``rotate_back`` false, the rotated-basis weight w8 * s_channel.  fp32 [N, K]."""
+    w8 = decode_w4(packed, srel_u8, codebook, group).astype(F32)
+    w_rot = (w8 * np.asarray(s_channel, dtype=F32)[:, None]).astype(F32)
+    return rotate_to_f32(w_rot, block) if rotate_back else w_rot
+
+
+def ste_weight_bf16(packed, srel_u8, s_channel, codebook, group: int = GROUP) -> np.ndarray:
+    """[AT] _w4a8_linear_ste_backward's weight: w8 and s_channel cast to bf16
+    (w8 exactly; s_channel rounded to nearest even), their product rounded to
+    bf16.  Returned as fp32 values [N, K] (each one a bf16 value)."""
+    w8 = decode_w4(packed, srel_u8, codebook, group).astype(F32)         # exact in bf16
+    s_b = bf16_bits_to_f32(f32_to_bf16_bits(np.asarray(s_channel, dtype=F32)))
+    prod = (w8 * s_b[:, None]).astype(F32)       # exact: 8 x 8 significant bits
+    return bf16_bits_to_f32(f32_to_bf16_bits(prod))
+
+
+def grad_input_exact(grad, w_bf16) -> np.ndarray:
+    """[AT] _w4a8_linear_ste_backward: grad [M, N] @ w [N, K], the straight-through
+    gradient with respect to the layer's (rotated) input.  Exact products of the
+    bf16 values summed in fp64 (the page's bf16 matmul accumulates in fp32 and
+    rounds to bf16; the comparison bound allows for both).  fp64 [M, K]."""
+    return np.asarray(grad, dtype=np.float64) @ np.asarray(w_bf16, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------
+# variants  ([H3] interleave_rows, swiglu_interleaved, QLinear::merge_loras)
+
+def interleave_rows(t) -> np.ndarray:
+    """[H3] interleave_rows: rows [a0 .. aF-1, b0 .. bF-1] -> [a0, b0, a1, b1, ...]
+    (a gate/up projection's outputs paired so SwiGLU reads neighbours)."""
+    t = np.asarray(t)
+    n = t.shape[0]
+    if n % 2:
+        raise ValueError("an even number of rows is needed")
+    return t.reshape((2, n // 2) + t.shape[1:]).swapaxes(0, 1).reshape(t.shape)
+
+
+def swiglu_interleaved(y) -> np.ndarray:
+    """[H3] swiglu_interleaved: for the last dimension laid out (g0, u0, g1, u1, ...),
+    silu(g) * u with silu(g) = g / (1 + exp(-g)); fp64 here (a reference for an
+    fp32 epilogue).  [..., 2F] -> [..., F]."""
+    y = np.asarray(y, dtype=np.float64)
+    g, u = y[..., 0::2], y[..., 1::2]
+    return g / (1.0 + np.exp(-g)) * u
+
+
+def lora_delta(a, b, scale) -> np.ndarray:
+    """[H3] QLinear::merge_loras delta of one adapter: scale * (B @ A), B [N, r],
+    A [r, K].  Reading: the products and their sum over r in fp64, in r order
+    (multiply, then add; no fused multiply-add), times the scale in fp64, rounded
+    once to fp32."""
+    a = np.asarray(a, dtype=F32).astype(np.float64)
+    b = np.asarray(b, dtype=F32).astype(np.float64)
+    acc = np.zeros((b.shape[0], a.shape[1]), dtype=np.float64)
+    for r in range(a.shape[0]):
+        acc = acc + b[:, r:r + 1] * a[r:r + 1, :]
+    return (acc * np.float64(np.float32(scale))).astype(F32)
+
+
+def lora_merge_weight(packed, srel_u8, s_channel, codebook, a, b, scale,
+                      block: int = ROT_BLOCK, group: int = GROUP) -> np.ndarray:
+    """[H3] QLinear::merge_loras for a ConvRot layer, in this format: dequantise
+    (dequantize_f32: w8 * s_channel rotated back to the plain basis), add the
+    adapter's delta (lora_delta) in fp32.  The result is the plain-basis fp32
+    weight that quantize_w4 (or requantize_codes) turns back into the layer."""
+    w = dequantize_f32(packed, srel_u8, s_channel, codebook, True, block, group)
+    return (w + lora_delta(a, b, scale)).astype(F32)
