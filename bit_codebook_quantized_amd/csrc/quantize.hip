@@ -29,125 +29,13 @@
 // group fits, which are deterministic, and writes codes and scales.  Rows with at most
 // 4096 columns keep the first pass's results in registers instead.
 #include "w4a8_device.hpp"
+#include "wquant_device.hpp"
 
 namespace w4a8 {
 namespace {
 
 constexpr int QZ_THREADS = 256;
 constexpr int QZ_CHUNK = 4096;   // columns per pass over a row
-constexpr int QTSTRIDE = 17;     // padded row of the fp64 transpose buffer
-
-__device__ __forceinline__ void qradix4(double& a0, double& a1, double& a2, double& a3) {
-    const double s = (a0 + a1) + (a2 + a3);
-    const double b0 = s - 2.0 * a3, b1 = s - 2.0 * a2, b2 = s - 2.0 * a1, b3 = s - 2.0 * a0;
-    a0 = b0; a1 = b1; a2 = b2; a3 = b3;
-}
-
-__device__ __forceinline__ void qradix16(double (&v)[16]) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) qradix4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) qradix4(v[g], v[g + 4], v[g + 8], v[g + 12]);
-}
-
-// fp32 -> OCP E4M3FN byte: round to nearest even on the mantissa, subnormals kept,
-// magnitudes above 464 (half-way past the largest finite value 448) and NaN give the
-// NaN byte.  Every scaling below is by a power of two, hence exact.
-__device__ __forceinline__ uint32_t f32_to_e4m3fn(float x) {
-    const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-    const float a = __builtin_fabsf(x);
-    if (!(a <= 464.0f)) return sign | 0x7Fu;               // NaN or too large
-    if (a < 0x1p-6f) return sign | (uint32_t)(int)__builtin_rintf(a * 512.0f);
-    int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;   // a = (1 + f) * 2^e
-    const float f = __uint_as_float(__float_as_uint(a) - ((uint32_t)e << 23)) - 1.0f;
-    int m = (int)__builtin_rintf(f * 8.0f);
-    if (m == 8) { m = 0; ++e; }
-    return sign | ((uint32_t)(e + 7) << 3) | (uint32_t)m;
-}
-
-// Nearest of 16 non-decreasing levels: p = count of levels < x, candidates p - 1 and
-// p clamped to 0..15, the upper one only if strictly closer (fp32 distances).
-// Returns the code; *lv receives the chosen level.
-__device__ __forceinline__ int nearest16(float x, const float (&lvl)[16], float* lv) {
-    int p = 0;
-    float lo = lvl[0], hi = lvl[15];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        if (lvl[c] < x) { ++p; lo = lvl[c]; }
-    }
-#pragma unroll
-    for (int c = 15; c >= 0; --c)
-        if (!(lvl[c] < x)) hi = lvl[c];
-    const int ilo = p > 0 ? p - 1 : 0, ihi = p < 15 ? p : 15;
-    const float dlo = __builtin_fabsf(__fsub_rn(x, lo)), dhi = __builtin_fabsf(__fsub_rn(x, hi));
-    const bool up = dhi < dlo;
-    *lv = up ? hi : lo;
-    return up ? ihi : ilo;
-}
-
-// Steps 1-3 on one group: returns gs; q / lv receive the codes and their levels.
-__device__ __forceinline__ float fit_group(const float (&w)[16], const float (&cb)[16], int (&q)[16],
-                                           float (&lv)[16]) {
-    const float tiny = 1e-8f;
-    float gs = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) gs = __builtin_fmaxf(gs, __builtin_fabsf(w[k]));
-    gs = __builtin_fmaxf(gs, tiny);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) q[k] = nearest16(__fdiv_rn(w[k], gs), cb, &lv[k]);
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        double num = 0.0, den = 0.0;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            num += (double)__fmul_rn(w[k], lv[k]);
-            den += (double)__fmul_rn(lv[k], lv[k]);
-        }
-        gs = __builtin_fmaxf(__fdiv_rn((float)num, __builtin_fmaxf((float)den, tiny)), tiny);
-#pragma unroll
-        for (int k = 0; k < 16; ++k) q[k] = nearest16(__fdiv_rn(w[k], gs), cb, &lv[k]);
-    }
-    return gs;
-}
-
-// Rotate (or load) the 16 columns of group `gi` of the current chunk into w.  All
-// threads call it (it synchronises).  Slot s of the block covers rotation block s of
-// the chunk; blocks past the row's end contribute zeros and are never stored.
-__device__ __forceinline__ void load_group(const float* __restrict__ wrow, int K, int c0, bool rotated, int slot,
-                                           int l16, double* tbuf, float* fbuf, float (&w)[16]) {
-    const int col = c0 + slot * 256 + l16 * 16;   // first column of this thread's 16
-    const bool ok = col < K;
-    float in[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float4 v = ok ? reinterpret_cast<const float4*>(wrow + col)[i] : float4{0.f, 0.f, 0.f, 0.f};
-        in[4 * i] = v.x; in[4 * i + 1] = v.y; in[4 * i + 2] = v.z; in[4 * i + 3] = v.w;
-    }
-    if (rotated) {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) w[k] = in[k];
-        return;
-    }
-    double v[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = (double)in[k];
-    qradix16(v);   // digits 0, 1 of the column within the block (inside the thread)
-    double* t = tbuf + slot * (16 * QTSTRIDE);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) t[l16 * QTSTRIDE + i] = v[i];
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = t[j * QTSTRIDE + l16];
-    __syncthreads();
-    qradix16(v);   // digits 2, 3; v[i] is now column 16*i + l16 of the block
-    float* f = fbuf + slot * (256 + 16);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) f[i * 17 + l16] = (float)(v[i] * 0.0625);
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 16; ++k) w[k] = f[l16 * 17 + k];
-    __syncthreads();
-}
 
 __global__ __launch_bounds__(QZ_THREADS) void quantize_kernel(const float* __restrict__ wt, int K, int rotated,
                                                               const float* __restrict__ codebook,
@@ -198,11 +86,7 @@ __global__ __launch_bounds__(QZ_THREADS) void quantize_kernel(const float* __res
             const uint32_t sb = f32_to_e4m3fn(__fdiv_rn(gs, sch));
             const float s = e4m3fn_to_f32(sb);
             float lvl[16];
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const float r = __builtin_rintf(__fmul_rn(cb[c], s));
-                lvl[c] = r < -127.0f ? -127.0f : (r > 127.0f ? 127.0f : r);   // NaN stays NaN
-            }
+            grid_levels16(cb, s, lvl);
             uint32_t packed[2] = {0u, 0u};
 #pragma unroll
             for (int k = 0; k < 16; ++k) {

@@ -1,0 +1,188 @@
+// Weight-side kernels of the training path, on a layer's stored scales (ai-toolkit
+// convrot_w4a8_quant.py, ConvRotW4A8Quantizer):
+//
+//   requantize_codes  -- requantize_codes_: new codes for an fp32 weight on the stored
+//                        group scales, channel scales and codebook.  The weight is
+//                        rotated (fp64 block rotation, rounded once to fp32) unless given
+//                        rotated; target = fp32(w_rot / s_channel); the code is the
+//                        nearest grid level (_assign_grid), or with uniform draws u the
+//                        stochastic choice between the two bracketing levels: with p the
+//                        count of levels below the target and lo = clamp(p - 1, 0, 14),
+//                        thr = fp32(fp32(u * fp32(lv[lo+1] - lv[lo])) + lv[lo]) and the
+//                        code is lo + (target > thr).
+//   fake_quant        -- fake_quant_rotated_weight: the nearest grid level of
+//                        fp32(w_rot / s_channel) times s_channel (fp32).
+//   dequantize        -- dequantize_w4a8: fp32(w8 * s_channel), rotated back to the plain
+//                        basis (the fp64 block sum of these terms is exact; rounded once).
+//
+// Layout: a block of 256 threads covers one 4096-column chunk of one row (grid =
+// rows x chunks); thread t holds the 16 columns of group t of the chunk, which is the
+// layout of the rotation helpers (slot t / 16 rotates block t / 16 of the chunk).
+// Fake quantisation needs no rotation and uses the same mapping.
+#include "w4a8_device.hpp"
+#include "wquant_device.hpp"
+
+namespace w4a8 {
+namespace {
+
+constexpr int RG_THREADS = 256;
+constexpr int RG_CHUNK = 4096;
+
+// Stochastic bracket choice ([AT] _assign_grid, stochastic branch) among 16
+// non-decreasing levels; comparisons with a NaN level are false.
+__device__ __forceinline__ uint32_t stochastic16(float x, float u, const float (&lvl)[16]) {
+    int p = 0;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) p += lvl[c] < x ? 1 : 0;
+    const int lo = p < 1 ? 0 : (p > 15 ? 14 : p - 1);
+    float l0 = lvl[0], l1 = lvl[1];
+#pragma unroll
+    for (int c = 1; c < 15; ++c) {
+        l0 = lo == c ? lvl[c] : l0;
+        l1 = lo == c ? lvl[c + 1] : l1;
+    }
+    const float thr = __fadd_rn(__fmul_rn(u, __fsub_rn(l1, l0)), l0);
+    return (uint32_t)(lo + (x > thr ? 1 : 0));
+}
+
+__device__ __forceinline__ void load16(const float* __restrict__ p, float (&v)[16]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float4 f = reinterpret_cast<const float4*>(p)[i];
+        v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+}
+
+__device__ __forceinline__ void store16(float* __restrict__ p, const float (&v)[16]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) reinterpret_cast<float4*>(p)[i] = float4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+}
+
+__global__ __launch_bounds__(RG_THREADS) void requant_kernel(const float* __restrict__ wt, int K, int nchunk,
+                                                             int rotated, const float* __restrict__ codebook,
+                                                             const uint8_t* __restrict__ srel,
+                                                             const float* __restrict__ s_channel,
+                                                             const float* __restrict__ u,
+                                                             uint8_t* __restrict__ qpacked) {
+    __shared__ double tbuf[16 * 16 * QTSTRIDE];
+    __shared__ float fbuf[16 * (256 + 16)];
+    const int tid = threadIdx.x, slot = tid >> 4, l16 = tid & 15;
+    const int64_t row = blockIdx.x / nchunk;
+    const int c0 = (blockIdx.x - (int)(row * nchunk)) * RG_CHUNK;
+    float w[16];
+    load_group(wt + row * K, K, c0, rotated != 0, slot, l16, tbuf, fbuf, w);   // block-uniform
+    const int col = c0 + tid * 16;
+    if (col >= K) return;
+    float cb[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) cb[c] = codebook[c];
+    const float sch = s_channel[row];
+    float lvl[16];
+    grid_levels16(cb, e4m3fn_to_f32(srel[row * (K >> 4) + (col >> 4)]), lvl);
+    float r[16];
+    if (u) load16(u + row * K + col, r);
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const float t = __fdiv_rn(w[k], sch);
+        uint32_t code;
+        if (u) {
+            code = stochastic16(t, r[k], lvl);
+        } else {
+            float dummy;
+            code = (uint32_t)nearest16(t, lvl, &dummy);
+        }
+        packed[k >> 3] |= code << (4 * (k & 7));
+    }
+    *reinterpret_cast<uint2*>(qpacked + row * (K >> 1) + (col >> 1)) = uint2{packed[0], packed[1]};
+}
+
+// One thread per 16-column group, no rotation.
+__global__ __launch_bounds__(RG_THREADS) void fake_quant_kernel(const float* __restrict__ w_rot, int64_t groups,
+                                                                int K, const float* __restrict__ codebook,
+                                                                const uint8_t* __restrict__ srel,
+                                                                const float* __restrict__ s_channel,
+                                                                float* __restrict__ out) {
+    const int64_t g = (int64_t)blockIdx.x * RG_THREADS + threadIdx.x;
+    if (g >= groups) return;
+    const int64_t row = g / (K >> 4);
+    float cb[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) cb[c] = codebook[c];
+    float lvl[16];
+    grid_levels16(cb, e4m3fn_to_f32(srel[g]), lvl);
+    const float sch = s_channel[row];
+    float w[16], y[16];
+    load16(w_rot + g * 16, w);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        float lv;
+        (void)nearest16(__fdiv_rn(w[k], sch), lvl, &lv);
+        y[k] = __fmul_rn(lv, sch);
+    }
+    store16(out + g * 16, y);
+}
+
+__global__ __launch_bounds__(RG_THREADS) void dequant_kernel(const uint8_t* __restrict__ qpacked,
+                                                             const uint8_t* __restrict__ srel,
+                                                             const float* __restrict__ codebook,
+                                                             const float* __restrict__ s_channel, int K, int nchunk,
+                                                             int rotate_back, float* __restrict__ out) {
+    __shared__ double tbuf[16 * 16 * QTSTRIDE];
+    __shared__ float fbuf[16 * (256 + 16)];
+    const int tid = threadIdx.x, slot = tid >> 4, l16 = tid & 15;
+    const int64_t row = blockIdx.x / nchunk;
+    const int c0 = (blockIdx.x - (int)(row * nchunk)) * RG_CHUNK;
+    const int col = c0 + tid * 16;
+    const bool ok = col < K;
+    float w[16];
+    if (ok) {
+        const float s = e4m3fn_to_f32(srel[row * (K >> 4) + (col >> 4)]);
+        const float sch = s_channel[row];
+        const uint2 q = *reinterpret_cast<const uint2*>(qpacked + row * (K >> 1) + (col >> 1));
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const uint32_t code = ((k < 8 ? q.x : q.y) >> (4 * (k & 7))) & 15u;
+            const float w8 = (float)(int8_t)(uint8_t)grid_level(codebook[code], s);
+            w[k] = __fmul_rn(w8, sch);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) w[k] = 0.0f;
+    }
+    if (rotate_back) rotate16_in_place(w, slot, l16, tbuf, fbuf);   // block-uniform
+    if (ok) store16(out + row * K + col, w);
+}
+
+}  // namespace
+
+hipError_t launch_requantize(const float* w, int64_t N, int K, int rotated, const float* codebook,
+                             const uint8_t* srel, const float* s_channel, const float* u, uint8_t* qpacked,
+                             hipStream_t stream) {
+    (void)hipGetLastError();   // clear a stale error so the check below is about this launch
+    const int nchunk = (K + RG_CHUNK - 1) / RG_CHUNK;
+    hipLaunchKernelGGL(requant_kernel, dim3((unsigned)(N * nchunk)), dim3(RG_THREADS), 0, stream, w, K, nchunk,
+                       rotated, codebook, srel, s_channel, u, qpacked);
+    return hipGetLastError();
+}
+
+hipError_t launch_fake_quant(const float* w_rot, int64_t N, int K, const float* codebook, const uint8_t* srel,
+                             const float* s_channel, float* out, hipStream_t stream) {
+    (void)hipGetLastError();
+    const int64_t groups = N * (K >> 4);
+    hipLaunchKernelGGL(fake_quant_kernel, dim3((unsigned)((groups + RG_THREADS - 1) / RG_THREADS)), dim3(RG_THREADS),
+                       0, stream, w_rot, groups, K, codebook, srel, s_channel, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* qpacked, const uint8_t* srel, const float* codebook,
+                             const float* s_channel, int64_t N, int K, int rotate_back, float* out,
+                             hipStream_t stream) {
+    (void)hipGetLastError();
+    const int nchunk = (K + RG_CHUNK - 1) / RG_CHUNK;
+    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)(N * nchunk)), dim3(RG_THREADS), 0, stream, qpacked, srel,
+                       codebook, s_channel, K, nchunk, rotate_back, out);
+    return hipGetLastError();
+}
+
+}  // namespace w4a8

@@ -24,6 +24,14 @@ hipError_t launch_gemv_act(const uint16_t* x, int M, int qmax, const uint8_t* qp
                            const float* codebook, const float* ws, const float* bias, int N, int K, int out_type,
                            void* out, int8_t* xq_out, float* xs_out, hipStream_t stream);
 int gemv_act_max_k(int M);
+hipError_t launch_requantize(const float* w, int64_t N, int K, int rotated, const float* codebook,
+                             const uint8_t* srel, const float* s_channel, const float* u, uint8_t* qpacked,
+                             hipStream_t stream);
+hipError_t launch_fake_quant(const float* w_rot, int64_t N, int K, const float* codebook, const uint8_t* srel,
+                             const float* s_channel, float* out, hipStream_t stream);
+hipError_t launch_dequantize(const uint8_t* qpacked, const uint8_t* srel, const float* codebook,
+                             const float* s_channel, int64_t N, int K, int rotate_back, float* out,
+                             hipStream_t stream);
 hipError_t launch_quantize(const float* w, int64_t N, int K, int rotated, const float* codebook, uint8_t* qpacked,
                            uint8_t* srel, float* s_channel, hipStream_t stream);
 }  // namespace w4a8
@@ -181,6 +189,60 @@ int quantize_w4(const float* w, int64_t N, int64_t K, int32_t rot_block, int32_t
                                           static_cast<hipStream_t>(stream)));
 }
 
+// Blocks of the row-chunk kernels (one per 4096 columns of a row) must fit a grid.
+int check_row_chunks(int64_t N, int64_t K) {
+    return N * ((K + 4095) / 4096) > INT32_MAX ? W4A8_ERR_SHAPE : W4A8_OK;
+}
+
+int requantize_codes_w4(const float* w, int64_t N, int64_t K, int32_t rot_block, int32_t group, int32_t rotated,
+                        const float* codebook, const uint8_t* srel, const float* s_channel, const float* u,
+                        uint8_t* qpacked, void* stream) {
+    int st = check_n(N);
+    if (st) return st;
+    if ((st = check_k(K))) return st;
+    if ((st = check_row_chunks(N, K))) return st;
+    if (rot_block != W4A8_ROT_BLOCK || group != W4A8_GROUP) return W4A8_ERR_UNSUPPORTED;
+    if (rotated != 0 && rotated != 1) return W4A8_ERR_INVALID_ARG;
+    if (!w || !codebook || !srel || !s_channel || !qpacked) return W4A8_ERR_INVALID_ARG;
+    if (!aligned(w, 16) || !aligned(codebook, 4) || !aligned(srel, 16) || !aligned(s_channel, 4) ||
+        !aligned(u, 16) || !aligned(qpacked, 16))
+        return W4A8_ERR_ALIGN;
+    return launched(w4a8::launch_requantize(w, N, (int)K, rotated, codebook, srel, s_channel, u, qpacked,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int fake_quant_w4(const float* w_rot, int64_t N, int64_t K, int32_t group, const float* codebook,
+                  const uint8_t* srel, const float* s_channel, float* out, void* stream) {
+    int st = check_n(N);
+    if (st) return st;
+    if ((st = check_k(K))) return st;
+    if ((st = check_row_chunks(N, K))) return st;
+    if (group != W4A8_GROUP) return W4A8_ERR_UNSUPPORTED;
+    if (!w_rot || !codebook || !srel || !s_channel || !out) return W4A8_ERR_INVALID_ARG;
+    if (!aligned(w_rot, 16) || !aligned(codebook, 4) || !aligned(srel, 16) || !aligned(s_channel, 4) ||
+        !aligned(out, 16))
+        return W4A8_ERR_ALIGN;
+    return launched(w4a8::launch_fake_quant(w_rot, N, (int)K, codebook, srel, s_channel, out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int dequantize_w4(const uint8_t* qpacked, const uint8_t* srel, const float* codebook, const float* s_channel,
+                  int64_t N, int64_t K, int32_t rot_block, int32_t group, int32_t rotate_back, float* out,
+                  void* stream) {
+    int st = check_n(N);
+    if (st) return st;
+    if ((st = check_k(K))) return st;
+    if ((st = check_row_chunks(N, K))) return st;
+    if (rot_block != W4A8_ROT_BLOCK || group != W4A8_GROUP) return W4A8_ERR_UNSUPPORTED;
+    if (rotate_back != 0 && rotate_back != 1) return W4A8_ERR_INVALID_ARG;
+    if (!qpacked || !srel || !codebook || !s_channel || !out) return W4A8_ERR_INVALID_ARG;
+    if (!aligned(qpacked, 16) || !aligned(srel, 16) || !aligned(codebook, 4) || !aligned(s_channel, 4) ||
+        !aligned(out, 16))
+        return W4A8_ERR_ALIGN;
+    return launched(w4a8::launch_dequantize(qpacked, srel, codebook, s_channel, N, (int)K, rotate_back, out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 const char* w4a8_status_string(int status) {
     switch (status) {
         case W4A8_OK: return "W4A8_OK";
@@ -193,6 +255,6 @@ const char* w4a8_status_string(int status) {
     }
 }
 
-int w4a8_abi_version(void) { return 4; }
+int w4a8_abi_version(void) { return 5; }
 
 }  // extern "C"

@@ -34,10 +34,8 @@ __device__ __forceinline__ uint32_t grid_level(float level, float scale) {
     return (uint32_t)((int32_t)r) & 0xFFu;
 }
 
-// Fill the LDS level table: lut[4*b + q] holds the levels of codes 4q..4q+3 for
-// scale byte b, one byte each (code 4q in the low byte).  All threads of the
-// block take part; the caller synchronises afterwards.
-// The same table from the 16 codebook values already in registers (uniform loads):
+// The level table (see build_level_table) from the 16 codebook values already in
+// registers (uniform loads):
 // nthreads must be a multiple of 4, so a thread's level quarter q is fixed.
 __device__ __forceinline__ void build_level_table_regs(uint32_t* lut, const float (&cb)[16], int tid, int nthreads) {
     const int q = tid & 3;
@@ -53,6 +51,9 @@ __device__ __forceinline__ void build_level_table_regs(uint32_t* lut, const floa
     }
 }
 
+// Fill the LDS level table: lut[4*b + q] holds the levels of codes 4q..4q+3 for
+// scale byte b, one byte each (code 4q in the low byte).  All threads of the
+// block take part; the caller synchronises afterwards.
 __device__ __forceinline__ void build_level_table(uint32_t* lut, const float* __restrict__ codebook,
                                                   int tid, int nthreads) {
     for (int i = tid; i < 1024; i += nthreads) {

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so"
 OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP = range(6)
 OUT_BF16, OUT_F32, OUT_I32 = 0, 1, 2
 ROT_BLOCK, GROUP, GEMV_MAX_M, MAX_K = 256, 16, 8, 131072
-ABI_VERSION = 4
+ABI_VERSION = 5
 FUSED_ACT_MAX_K = 4096   # linear() uses w4a8_gemv_act for one row up to this K
 _OUT_CODES = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32, torch.int32: OUT_I32}
 
@@ -47,6 +47,9 @@ SIGNATURES = {
     "w4a8_gemv_grouped": [_P, _I32, _I64, _I32, _I32, _P],
     "w4a8_gemv_act": [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _P, _P],
     "w4a8_gemv_act_max_k": [_I64],
+    "requantize_codes_w4": [_P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P],
+    "fake_quant_w4": [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P],
+    "dequantize_w4": [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P],
     "w4a8_status_string": [ctypes.c_int],
     "w4a8_abi_version": [],
 }
@@ -319,6 +322,54 @@ def quantize_w4(w: torch.Tensor, codebook=None, rotated: bool = False, bias=None
     if bias is not None:
         bias = _dev(bias, torch.float32, "bias")
     return W4A8Layer(qp, sr, cb, sch, bias)
+
+
+def requantize_codes(w: torch.Tensor, layer: W4A8Layer, rotated: bool = False, u: torch.Tensor = None,
+                     out: torch.Tensor = None) -> torch.Tensor:
+    """New packed codes [N, K/2] for the fp32 weight w [N, K] on the layer's stored
+    scales (the layer is not modified): nearest grid level, or with uniform draws
+    u [N, K] in [0, 1) the unbiased stochastic choice between bracketing levels."""
+    layer.check()
+    _dev(w, torch.float32, "w")
+    n, k = w.shape
+    if (n, k) != (layer.out_features, layer.in_features):
+        raise ValueError(f"w is {tuple(w.shape)}, the layer is {layer.out_features}x{layer.in_features}")
+    if u is not None:
+        _dev(u, torch.float32, "u")
+        if tuple(u.shape) != (n, k):
+            raise ValueError("u must have the weight's shape")
+    out = _out(out, (n, k // 2), torch.uint8, w.device, "out")
+    _check("requantize_codes_w4", load().requantize_codes_w4(
+        w.data_ptr(), n, k, ROT_BLOCK, GROUP, int(bool(rotated)), layer.codebook.data_ptr(), layer.srel.data_ptr(),
+        layer.s_channel.data_ptr(), None if u is None else u.data_ptr(), out.data_ptr(), _stream(w)))
+    return out
+
+
+def fake_quant(w_rot: torch.Tensor, layer: W4A8Layer, out: torch.Tensor = None) -> torch.Tensor:
+    """dequant(quant(w_rot)) on the layer's stored scales, fp32 [N, K]."""
+    layer.check()
+    _dev(w_rot, torch.float32, "w_rot")
+    n, k = w_rot.shape
+    if (n, k) != (layer.out_features, layer.in_features):
+        raise ValueError(f"w_rot is {tuple(w_rot.shape)}, the layer is {layer.out_features}x{layer.in_features}")
+    out = _out(out, (n, k), torch.float32, w_rot.device, "out")
+    _check("fake_quant_w4", load().fake_quant_w4(w_rot.data_ptr(), n, k, GROUP, layer.codebook.data_ptr(),
+                                                 layer.srel.data_ptr(), layer.s_channel.data_ptr(), out.data_ptr(),
+                                                 _stream(w_rot)))
+    return out
+
+
+def dequantize(layer: W4A8Layer, rotate_back: bool = True, out: torch.Tensor = None) -> torch.Tensor:
+    """The layer's weight in fp32 [N, K]: w8 * s_channel, rotated back to the plain
+    basis unless rotate_back is false."""
+    layer.check()
+    n, k = layer.out_features, layer.in_features
+    out = _out(out, (n, k), torch.float32, layer.qpacked.device, "out")
+    _check("dequantize_w4", load().dequantize_w4(layer.qpacked.data_ptr(), layer.srel.data_ptr(),
+                                                 layer.codebook.data_ptr(), layer.s_channel.data_ptr(), n, k,
+                                                 ROT_BLOCK, GROUP, int(bool(rotate_back)), out.data_ptr(),
+                                                 _stream(layer.qpacked)))
+    return out
 
 
 def linear(x: torch.Tensor, layer: W4A8Layer, out_dtype=torch.bfloat16) -> torch.Tensor:

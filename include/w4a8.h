@@ -225,6 +225,62 @@ int w4a8_gemv_grouped(const w4a8_gemv_layer* layers, int32_t count, int64_t M, i
 int quantize_w4(const float* w, int64_t N, int64_t K, int32_t rot_block, int32_t group, int32_t rotated,
                 const float* codebook, uint8_t* qpacked, uint8_t* srel, float* s_channel, void* stream);
 
+/*
+ * requantize_codes_w4 -- new 4-bit codes for an fp32 weight on a layer's STORED group
+ * scales, channel scales and codebook (ai-toolkit ConvRotW4A8Quantizer.requantize_codes_,
+ * the grid a quantisation-aware run trains against, with _assign_grid):
+ *   w_rot  = the weight rotated like quantize_w4 (unless `rotated`);
+ *   target = fp32(w_rot / s_channel[n]);
+ *   levels = clamp(rint(fp32(codebook[c] * e4m3(srel[n, k/16]))), -127, 127);
+ *   code   = the nearest level (left insertion point p, upper candidate only if strictly
+ *            closer) -- or, when u is not NULL, the unbiased stochastic choice between
+ *            the bracketing levels: lo = clamp(p - 1, 0, 14),
+ *            thr = fp32(fp32(u * fp32(level[lo+1] - level[lo])) + level[lo]),
+ *            code = lo + (target > thr).
+ * The codebook must be sorted ascending (the levels are then non-decreasing).
+ *
+ *   w            in   float [N, K], the weight (plain basis, or rotated if `rotated`)
+ *   N, K, rot_block, group   as for quantize_w4
+ *   rotated           0 or 1
+ *   codebook, srel,   in   the layer's stored codebook [16], scale bytes [N, K/16] and
+ *   s_channel              channel scales [N]
+ *   u            in   NULL (nearest) or float [N, K] uniform draws in [0, 1) (the page
+ *                     draws them with rand_like; they are inputs here)
+ *   qpacked      out  uint8 [N, K/2], the new codes (the scales are not written)
+ */
+int requantize_codes_w4(const float* w, int64_t N, int64_t K, int32_t rot_block, int32_t group, int32_t rotated,
+                        const float* codebook, const uint8_t* srel, const float* s_channel, const float* u,
+                        uint8_t* qpacked, void* stream);
+
+/*
+ * fake_quant_w4 -- ai-toolkit ConvRotW4A8Quantizer.fake_quant_rotated_weight:
+ * dequant(quant(w_rot)) on the stored scales, out[n, k] = fp32(level * s_channel[n])
+ * with level the nearest grid level of fp32(w_rot[n, k] / s_channel[n]) (as in
+ * requantize_codes_w4).
+ *
+ *   w_rot        in   float [N, K], the weight in the rotated basis
+ *   N, K, group       sizes; group must be 16
+ *   codebook, srel, s_channel   in   the layer's stored codebook, scale bytes, channel scales
+ *   out          out  float [N, K] (may not overlap w_rot)
+ */
+int fake_quant_w4(const float* w_rot, int64_t N, int64_t K, int32_t group, const float* codebook,
+                  const uint8_t* srel, const float* s_channel, float* out, void* stream);
+
+/*
+ * dequantize_w4 -- ai-toolkit dequantize_w4a8: the layer's weight in fp32,
+ * out = fp32(w8 * s_channel[n]) with w8 the decoded int8 grid (as decode_w4_to_int8),
+ * rotated back to the plain basis when `rotate_back` (each 256-column block times
+ * H4^(x4) / 16; the exact block sum rounded once to fp32), else left rotated.
+ *
+ *   qpacked, srel, codebook, s_channel   in   the layer storage
+ *   N, K, rot_block, group                    sizes; rot_block 256, group 16
+ *   rotate_back                               0 or 1
+ *   out                                  out  float [N, K]
+ */
+int dequantize_w4(const uint8_t* qpacked, const uint8_t* srel, const float* codebook, const float* s_channel,
+                  int64_t N, int64_t K, int32_t rot_block, int32_t group, int32_t rotate_back, float* out,
+                  void* stream);
+
 /* Name of a status code ("W4A8_OK", ...); never NULL. */
 const char* w4a8_status_string(int status);
 

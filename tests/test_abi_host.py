@@ -28,9 +28,10 @@ def w4a8():
 def test_header_declares_the_operations():
     names = _declared_functions()
     for n in ("rotate_quant_act", "decode_w4_to_int8", "w4a8_gemm", "w4a8_gemv", "w4a8_gemv_grouped",
-              "quantize_w4", "w4a8_gemv_act", "w4a8_gemv_act_max_k", "w4a8_status_string", "w4a8_abi_version"):
+              "quantize_w4", "w4a8_gemv_act", "w4a8_gemv_act_max_k", "requantize_codes_w4", "fake_quant_w4",
+              "dequantize_w4", "w4a8_status_string", "w4a8_abi_version"):
         assert n in names
-    assert len(names) == 10, names
+    assert len(names) == 13, names
 
 
 def test_library_exports_every_declared_symbol(w4a8):
@@ -45,7 +46,7 @@ def test_status_strings(w4a8):
         "W4A8_OK", "W4A8_ERR_INVALID_ARG", "W4A8_ERR_SHAPE", "W4A8_ERR_ALIGN", "W4A8_ERR_UNSUPPORTED",
         "W4A8_ERR_HIP"]
     assert w4a8.status_string(99) == "W4A8_ERR_UNKNOWN"
-    assert w4a8.load().w4a8_abi_version() == w4a8.ABI_VERSION == 4
+    assert w4a8.load().w4a8_abi_version() == w4a8.ABI_VERSION == 5
 
 
 A = 1 << 20          # a 16-byte-aligned fake address (never dereferenced: validation fails first)
@@ -118,6 +119,40 @@ def test_gemv_act_validation(w4a8):
         assert _act(w4a8, **kw) == w4a8.ERR_ALIGN, p
     assert _act(w4a8, xq_out=A, xs_out=A + 2) == w4a8.ERR_ALIGN
     assert _act(w4a8, M=0, x=None, out=None, qp=U) == w4a8.ERR_ALIGN
+
+
+def test_regrid_validation(w4a8):
+    def rq(**kw):
+        a = dict(w=A, N=4, K=256, rot=256, group=16, rotated=0, cb=A, srel=A, sch=A, u=None, out=A)
+        a.update(kw)
+        return w4a8.call("requantize_codes_w4", a["w"], a["N"], a["K"], a["rot"], a["group"], a["rotated"], a["cb"],
+                         a["srel"], a["sch"], a["u"], a["out"], None)
+
+    def fq(**kw):
+        a = dict(w=A, N=4, K=256, group=16, cb=A, srel=A, sch=A, out=A)
+        a.update(kw)
+        return w4a8.call("fake_quant_w4", a["w"], a["N"], a["K"], a["group"], a["cb"], a["srel"], a["sch"], a["out"],
+                         None)
+
+    def dq(**kw):
+        a = dict(qp=A, srel=A, cb=A, sch=A, N=4, K=256, rot=256, group=16, back=1, out=A)
+        a.update(kw)
+        return w4a8.call("dequantize_w4", a["qp"], a["srel"], a["cb"], a["sch"], a["N"], a["K"], a["rot"], a["group"],
+                         a["back"], a["out"], None)
+
+    for f in (rq, fq, dq):
+        assert f(N=0) == w4a8.ERR_SHAPE
+        assert f(N=-1) == w4a8.ERR_INVALID_ARG
+        assert f(K=300) == w4a8.ERR_SHAPE
+        assert f(group=32) == w4a8.ERR_UNSUPPORTED
+        assert f(cb=None) == w4a8.ERR_INVALID_ARG
+        assert f(sch=A + 2) == w4a8.ERR_ALIGN
+        assert f(out=A + 8) == w4a8.ERR_ALIGN
+        assert f(N=1 << 30, K=131072) == w4a8.ERR_SHAPE       # more row chunks than a grid holds
+    assert rq(rot=128) == w4a8.ERR_UNSUPPORTED and dq(rot=128) == w4a8.ERR_UNSUPPORTED
+    assert rq(rotated=2) == w4a8.ERR_INVALID_ARG and dq(back=2) == w4a8.ERR_INVALID_ARG
+    assert rq(u=A + 4) == w4a8.ERR_ALIGN and rq(w=A + 4) == w4a8.ERR_ALIGN and fq(w=A + 4) == w4a8.ERR_ALIGN
+    assert rq(w=None) == w4a8.ERR_INVALID_ARG and fq(w=None) == w4a8.ERR_INVALID_ARG and dq(qp=None) == w4a8.ERR_INVALID_ARG
 
 
 def test_rotate_quant_validation(w4a8):
