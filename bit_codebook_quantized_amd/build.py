@@ -12,7 +12,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libw4a8.so")
-SOURCES = ["w4a8_api.cpp", "rotate_quant.hip", "decode.hip", "gemv.hip", "gemm.hip", "quantize.hip", "regrid.hip"]
+SOURCES = ["w4a8_api.cpp", "rotate_quant.hip", "decode.hip", "gemv.hip", "gemm.hip", "quantize.hip", "regrid.hip", "grad.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

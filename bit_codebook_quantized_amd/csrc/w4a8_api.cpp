@@ -29,6 +29,8 @@ hipError_t launch_requantize(const float* w, int64_t N, int K, int rotated, cons
                              hipStream_t stream);
 hipError_t launch_fake_quant(const float* w_rot, int64_t N, int K, const float* codebook, const uint8_t* srel,
                              const float* s_channel, float* out, hipStream_t stream);
+hipError_t launch_grad_input(const uint16_t* grad, int M, int N, int K, const uint8_t* qp, const uint8_t* srel,
+                             const float* codebook, const float* s_channel, uint16_t* out, hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t* qpacked, const uint8_t* srel, const float* codebook,
                              const float* s_channel, int64_t N, int K, int rotate_back, float* out,
                              hipStream_t stream);
@@ -243,6 +245,28 @@ int dequantize_w4(const uint8_t* qpacked, const uint8_t* srel, const float* code
                                             static_cast<hipStream_t>(stream)));
 }
 
+int w4a8_grad_input(const void* grad, int64_t M, const uint8_t* qpacked, const uint8_t* srel,
+                    const float* codebook, const float* s_channel, int64_t N, int64_t K, int32_t group, void* out,
+                    void* stream) {
+    if (M < 0) return W4A8_ERR_INVALID_ARG;
+    if (M > MAX_ROWS) return W4A8_ERR_SHAPE;
+    int st = check_n(N);
+    if (st) return st;
+    if ((st = check_k(K))) return st;
+    if (N % 8 != 0) return W4A8_ERR_SHAPE;
+    if (((M + 127) / 128) * (K / 128) > INT32_MAX) return W4A8_ERR_SHAPE;   // output tile count
+    if (group != W4A8_GROUP) return W4A8_ERR_UNSUPPORTED;
+    if (!qpacked || !srel || !codebook || !s_channel) return W4A8_ERR_INVALID_ARG;
+    if (M > 0 && (!grad || !out)) return W4A8_ERR_INVALID_ARG;
+    if (!aligned(qpacked, 16) || !aligned(srel, 16) || !aligned(codebook, 4) || !aligned(s_channel, 4))
+        return W4A8_ERR_ALIGN;
+    if (M > 0 && (!aligned(grad, 16) || !aligned(out, 16))) return W4A8_ERR_ALIGN;
+    if (M == 0) return W4A8_OK;
+    return launched(w4a8::launch_grad_input(static_cast<const uint16_t*>(grad), (int)M, (int)N, (int)K, qpacked,
+                                            srel, codebook, s_channel, static_cast<uint16_t*>(out),
+                                            static_cast<hipStream_t>(stream)));
+}
+
 const char* w4a8_status_string(int status) {
     switch (status) {
         case W4A8_OK: return "W4A8_OK";
@@ -255,6 +279,6 @@ const char* w4a8_status_string(int status) {
     }
 }
 
-int w4a8_abi_version(void) { return 5; }
+int w4a8_abi_version(void) { return 6; }
 
 }  // extern "C"

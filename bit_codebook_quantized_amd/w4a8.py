@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so"
 OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP = range(6)
 OUT_BF16, OUT_F32, OUT_I32 = 0, 1, 2
 ROT_BLOCK, GROUP, GEMV_MAX_M, MAX_K = 256, 16, 8, 131072
-ABI_VERSION = 5
+ABI_VERSION = 6
 FUSED_ACT_MAX_K = 4096   # linear() uses w4a8_gemv_act for one row up to this K
 _OUT_CODES = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32, torch.int32: OUT_I32}
 
@@ -50,6 +50,7 @@ SIGNATURES = {
     "requantize_codes_w4": [_P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P],
     "fake_quant_w4": [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P],
     "dequantize_w4": [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P],
+    "w4a8_grad_input": [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I32, _P, _P],
     "w4a8_status_string": [ctypes.c_int],
     "w4a8_abi_version": [],
 }
@@ -369,6 +370,22 @@ def dequantize(layer: W4A8Layer, rotate_back: bool = True, out: torch.Tensor = N
                                                  layer.codebook.data_ptr(), layer.s_channel.data_ptr(), n, k,
                                                  ROT_BLOCK, GROUP, int(bool(rotate_back)), out.data_ptr(),
                                                  _stream(layer.qpacked)))
+    return out
+
+
+def grad_input(grad: torch.Tensor, layer: W4A8Layer, out: torch.Tensor = None) -> torch.Tensor:
+    """The straight-through backward: bf16 grad [M, N] -> bf16 grad_x [M, K] with respect
+    to the layer's rotated input (grad @ (w8 * s_channel) in bf16, fp32 accumulation)."""
+    layer.check()
+    _dev(grad, torch.bfloat16, "grad")
+    m, n = grad.shape
+    if n != layer.out_features:
+        raise ValueError(f"grad has N={n}, the layer has N={layer.out_features}")
+    out = _out(out, (m, layer.in_features), torch.bfloat16, grad.device, "out")
+    _check("w4a8_grad_input", load().w4a8_grad_input(grad.data_ptr(), m, layer.qpacked.data_ptr(),
+                                                     layer.srel.data_ptr(), layer.codebook.data_ptr(),
+                                                     layer.s_channel.data_ptr(), n, layer.in_features, GROUP,
+                                                     out.data_ptr(), _stream(grad)))
     return out
 
 

@@ -49,7 +49,8 @@ extern "C" {
 enum w4a8_status {
     W4A8_OK = 0,
     W4A8_ERR_INVALID_ARG = 1,  /* NULL required pointer, negative size, unknown out_type */
-    W4A8_ERR_SHAPE = 2,        /* N < 1, K not a positive multiple of 256, K > W4A8_MAX_K */
+    W4A8_ERR_SHAPE = 2,        /* N < 1, K not a positive multiple of 256, K > W4A8_MAX_K,
+                                  N not a multiple of 8 for w4a8_grad_input */
     W4A8_ERR_ALIGN = 3,        /* a pointer misses its required alignment */
     W4A8_ERR_UNSUPPORTED = 4,  /* group != 16, rot_block != 256, qmax not in 1..127,
                                   M > W4A8_GEMV_MAX_M for the GEMV entry points,
@@ -280,6 +281,27 @@ int fake_quant_w4(const float* w_rot, int64_t N, int64_t K, int32_t group, const
 int dequantize_w4(const uint8_t* qpacked, const uint8_t* srel, const float* codebook, const float* s_channel,
                   int64_t N, int64_t K, int32_t rot_block, int32_t group, int32_t rotate_back, float* out,
                   void* stream);
+
+/*
+ * w4a8_grad_input -- the straight-through backward of the layer (ai-toolkit
+ * _w4a8_linear_ste_backward): grad_x = grad @ w with
+ *   w[n, k] = bf16(bf16(w8[n, k]) * bf16(s_channel[n]))      (each cast round-to-nearest-even)
+ * the decoded int8 grid times the channel scale in bf16; products accumulated in fp32
+ * on the matrix cores, the result rounded to bf16.  The gradient is with respect to the
+ * layer's rotated input xr (the input of step 2 above), as on the page; the gradient
+ * with respect to x is its block rotation (the rotation is its own inverse).  The weight
+ * is decoded on chip; nothing but grad_x is written.
+ *
+ *   grad                in   bf16 bits [M, N], the gradient of the layer's output
+ *   M                        rows, >= 0
+ *   qpacked, srel,      in   the layer storage
+ *   codebook, s_channel
+ *   N, K, group              N must be a multiple of 8 (16-byte rows of grad); group 16
+ *   out                 out  bf16 bits [M, K]
+ */
+int w4a8_grad_input(const void* grad, int64_t M, const uint8_t* qpacked, const uint8_t* srel,
+                    const float* codebook, const float* s_channel, int64_t N, int64_t K, int32_t group,
+                    void* out, void* stream);
 
 /* Name of a status code ("W4A8_OK", ...); never NULL. */
 const char* w4a8_status_string(int status);

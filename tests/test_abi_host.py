@@ -29,9 +29,9 @@ def test_header_declares_the_operations():
     names = _declared_functions()
     for n in ("rotate_quant_act", "decode_w4_to_int8", "w4a8_gemm", "w4a8_gemv", "w4a8_gemv_grouped",
               "quantize_w4", "w4a8_gemv_act", "w4a8_gemv_act_max_k", "requantize_codes_w4", "fake_quant_w4",
-              "dequantize_w4", "w4a8_status_string", "w4a8_abi_version"):
+              "dequantize_w4", "w4a8_grad_input", "w4a8_status_string", "w4a8_abi_version"):
         assert n in names
-    assert len(names) == 13, names
+    assert len(names) == 14, names
 
 
 def test_library_exports_every_declared_symbol(w4a8):
@@ -46,7 +46,7 @@ def test_status_strings(w4a8):
         "W4A8_OK", "W4A8_ERR_INVALID_ARG", "W4A8_ERR_SHAPE", "W4A8_ERR_ALIGN", "W4A8_ERR_UNSUPPORTED",
         "W4A8_ERR_HIP"]
     assert w4a8.status_string(99) == "W4A8_ERR_UNKNOWN"
-    assert w4a8.load().w4a8_abi_version() == w4a8.ABI_VERSION == 5
+    assert w4a8.load().w4a8_abi_version() == w4a8.ABI_VERSION == 6
 
 
 A = 1 << 20          # a 16-byte-aligned fake address (never dereferenced: validation fails first)
@@ -153,6 +153,24 @@ def test_regrid_validation(w4a8):
     assert rq(rotated=2) == w4a8.ERR_INVALID_ARG and dq(back=2) == w4a8.ERR_INVALID_ARG
     assert rq(u=A + 4) == w4a8.ERR_ALIGN and rq(w=A + 4) == w4a8.ERR_ALIGN and fq(w=A + 4) == w4a8.ERR_ALIGN
     assert rq(w=None) == w4a8.ERR_INVALID_ARG and fq(w=None) == w4a8.ERR_INVALID_ARG and dq(qp=None) == w4a8.ERR_INVALID_ARG
+
+
+def test_grad_input_validation(w4a8):
+    def gi(**kw):
+        a = dict(g=A, M=4, qp=A, srel=A, cb=A, sch=A, N=64, K=256, group=16, out=A)
+        a.update(kw)
+        return w4a8.call("w4a8_grad_input", a["g"], a["M"], a["qp"], a["srel"], a["cb"], a["sch"], a["N"], a["K"],
+                         a["group"], a["out"], None)
+
+    assert gi(M=-1) == w4a8.ERR_INVALID_ARG
+    assert gi(N=60) == w4a8.ERR_SHAPE                 # rows of grad must be 16-byte multiples
+    assert gi(N=0) == w4a8.ERR_SHAPE and gi(K=300) == w4a8.ERR_SHAPE
+    assert gi(group=32) == w4a8.ERR_UNSUPPORTED
+    for p in ("qp", "srel", "cb", "sch", "g", "out"):
+        assert gi(**{p: None}) == w4a8.ERR_INVALID_ARG, p
+    for p in ("g", "out", "qp", "srel"):
+        assert gi(**{p: A + 8}) == w4a8.ERR_ALIGN, p
+    assert gi(M=0, g=None, out=None, qp=U) == w4a8.ERR_ALIGN
 
 
 def test_rotate_quant_validation(w4a8):
