@@ -264,7 +264,17 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
                 if (bias) y[r] = __fadd_rn(y[r], bsv[r]);
             }
             const int64_t idx = (int64_t)m * N + n;
-            if (vec) {
+            if (OUT == 3) {
+                // gate/up pairs (n, n + 1) and (n + 2, n + 3) -> columns n/2, n/2 + 1 of [M, N/2]
+                uint16_t* o = reinterpret_cast<uint16_t*>(out) + (int64_t)m * (N >> 1) + (n >> 1);
+                const uint16_t s0 = f32_to_bf16(swiglu_f32(y[0], y[1])), s1 = f32_to_bf16(swiglu_f32(y[2], y[3]));
+                if (vec) {
+                    *reinterpret_cast<uint32_t*>(o) = (uint32_t)s0 | ((uint32_t)s1 << 16);
+                } else if (m < M) {
+                    if (n + 1 < N) o[0] = s0;
+                    if (n + 3 < N) o[1] = s1;
+                }
+            } else if (vec) {
                 if (OUT == 0) {
                     uint2 p;
                     p.x = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
@@ -298,6 +308,9 @@ hipError_t launch_gemm(const int8_t* xq, const float* xs, int M, const uint8_t* 
                            tiles_m, tiles_n);
     else if (out_type == 1)
         hipLaunchKernelGGL(gemm_kernel<1>, g, b, 0, stream, xq, xs, M, qp, srel, codebook, ws, bias, N, K, out,
+                           tiles_m, tiles_n);
+    else if (out_type == 3)
+        hipLaunchKernelGGL(gemm_kernel<3>, g, b, 0, stream, xq, xs, M, qp, srel, codebook, ws, bias, N, K, out,
                            tiles_m, tiles_n);
     else
         hipLaunchKernelGGL(gemm_kernel<2>, g, b, 0, stream, xq, xs, M, qp, srel, codebook, ws, bias, N, K, out,

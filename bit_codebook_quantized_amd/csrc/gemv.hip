@@ -385,9 +385,16 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
             }
             const float xm = xs_lds[m < MM ? m : 0];
             const int n = n0 + r;
-            if ((lane & ((1 << (6 - L)) - 1)) == 0 && idx < V && n < N) {
-                float y = __fmul_rn((float)v[0], __fmul_rn(xm, wn));
-                if (bias) y = __fadd_rn(y, bn);
+            const bool lead = (lane & ((1 << (6 - L)) - 1)) == 0 && idx < V && n < N;
+            float y = __fmul_rn((float)v[0], __fmul_rn(xm, wn));
+            if (bias) y = __fadd_rn(y, bn);
+            if (out_type == 3) {
+                // SwiGLU (two rows per wave): the gate row n0 (r = 0) takes the up row n0 + 1
+                // from the lane holding (r = 1, m), MM values further on
+                const float u = __shfl(y, lane + (MM << (6 - L)), 64);
+                if (lead && r == 0)
+                    reinterpret_cast<uint16_t*>(out)[(int64_t)m * (N >> 1) + (n >> 1)] = f32_to_bf16(swiglu_f32(y, u));
+            } else if (lead) {
                 store_out(out, out_type, (int64_t)m * N + n, v[0], y);
             }
         }
@@ -461,7 +468,7 @@ template <int MM>
 hipError_t launch_gemv_grouped_m(const w4a8_gemv_layer* layers, int count, int out_type, hipStream_t stream) {
     int64_t rows = 0;
     for (int i = 0; i < count; ++i) rows += layers[i].N;
-    const int R = rows_per_wave(rows), per_tile = (GV_THREADS / 64) * R;
+    const int R = out_type == 3 ? 2 : rows_per_wave(rows), per_tile = (GV_THREADS / 64) * R;   // SwiGLU pairs rows
     // consecutive row tiles per block: enough blocks for a few rounds over the chip
     // (256 compute units x 3 resident blocks x 4), fewer level-table builds per row
     const int64_t total_tiles = (rows + per_tile - 1) / per_tile + count;
@@ -494,7 +501,7 @@ hipError_t launch_gemv_m(const int8_t* xq, const float* xs, const uint8_t* qp, c
                          const float* codebook, const float* ws, const float* bias, int N, int K, int out_type,
                          void* out, hipStream_t stream) {
     const int waves_per_block = GV_THREADS / 64;
-    const int R = rows_per_wave(N);
+    const int R = out_type == 3 ? 2 : rows_per_wave(N);   // SwiGLU pairs the rows of a wave
     const int blocks = (N + waves_per_block * R - 1) / (waves_per_block * R);
     const size_t lds = gemv_lds_bytes(MM, false);
     const dim3 g(blocks), b(GV_THREADS);
@@ -512,7 +519,7 @@ hipError_t launch_gemv_act_m(const uint16_t* x, int qmax, const uint8_t* qp, con
                              const float* codebook, const float* ws, const float* bias, int N, int K, int out_type,
                              void* out, int8_t* xq_out, float* xs_out, hipStream_t stream) {
     const int waves_per_block = GV_THREADS / 64;
-    const int R = rows_per_wave(N);
+    const int R = out_type == 3 ? 2 : rows_per_wave(N);   // SwiGLU pairs the rows of a wave
     const int blocks = (N + waves_per_block * R - 1) / (waves_per_block * R);
     const size_t lds = gemv_lds_bytes(MM, true);
     const dim3 g(blocks), b(GV_THREADS);

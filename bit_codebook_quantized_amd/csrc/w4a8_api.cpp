@@ -68,7 +68,8 @@ int check_linear(const int8_t* xq, const float* xs, int64_t M, const uint8_t* qp
     int st = check_n(N);
     if (st) return st;
     if ((st = check_k(K))) return st;
-    if (out_type < W4A8_OUT_BF16 || out_type > W4A8_OUT_I32) return W4A8_ERR_INVALID_ARG;
+    if (out_type < W4A8_OUT_BF16 || out_type > W4A8_OUT_SWIGLU_BF16) return W4A8_ERR_INVALID_ARG;
+    if (out_type == W4A8_OUT_SWIGLU_BF16 && N % 2 != 0) return W4A8_ERR_SHAPE;
     if (group != W4A8_GROUP) return W4A8_ERR_UNSUPPORTED;
     if (!qpacked || !srel || !codebook || !s_channel) return W4A8_ERR_INVALID_ARG;
     if (M > 0 && (!xq || !xs || !out)) return W4A8_ERR_INVALID_ARG;
@@ -139,7 +140,8 @@ int w4a8_gemv_act(const void* x, int64_t M, int32_t rot_block, int32_t qmax, con
     int st = check_n(N);
     if (st) return st;
     if ((st = check_k(K))) return st;
-    if (out_type < W4A8_OUT_BF16 || out_type > W4A8_OUT_I32) return W4A8_ERR_INVALID_ARG;
+    if (out_type < W4A8_OUT_BF16 || out_type > W4A8_OUT_SWIGLU_BF16) return W4A8_ERR_INVALID_ARG;
+    if (out_type == W4A8_OUT_SWIGLU_BF16 && N % 2 != 0) return W4A8_ERR_SHAPE;
     if (group != W4A8_GROUP || rot_block != W4A8_ROT_BLOCK || qmax < 1 || qmax > 127) return W4A8_ERR_UNSUPPORTED;
     if (M > W4A8_GEMV_MAX_M) return W4A8_ERR_UNSUPPORTED;
     if (!qpacked || !srel || !codebook || !s_channel) return W4A8_ERR_INVALID_ARG;
@@ -279,6 +281,6 @@ const char* w4a8_status_string(int status) {
     }
 }
 
-int w4a8_abi_version(void) { return 6; }
+int w4a8_abi_version(void) { return 7; }
 
 }  // extern "C"

@@ -105,6 +105,12 @@ __device__ __forceinline__ float epilogue_f32(int32_t acc, float xs, float ws, c
     return y;
 }
 
+// SwiGLU of one gate/up pair (h3-rs 0.2.0 src/weights.rs, swiglu_interleaved):
+// silu(g) * u = g / (1 + exp(-g)) * u in fp32, each operation rounded on its own.
+__device__ __forceinline__ float swiglu_f32(float g, float u) {
+    return __fmul_rn(__fdiv_rn(g, __fadd_rn(1.0f, expf(-g))), u);
+}
+
 __device__ __forceinline__ void store_out(void* out, int out_type, int64_t idx, int32_t acc, float y) {
     if (out_type == 0) {
         reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16(y);

@@ -21,11 +21,23 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8.so")
 
 OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP = range(6)
-OUT_BF16, OUT_F32, OUT_I32 = 0, 1, 2
+OUT_BF16, OUT_F32, OUT_I32, OUT_SWIGLU = 0, 1, 2, 3
+# out_dtype value of the SwiGLU epilogue: bf16 [M, N/2] = silu(gate) * up on
+# gate/up-interleaved rows
+SWIGLU = "swiglu"
 ROT_BLOCK, GROUP, GEMV_MAX_M, MAX_K = 256, 16, 8, 131072
-ABI_VERSION = 6
+ABI_VERSION = 7
 FUSED_ACT_MAX_K = 4096   # linear() uses w4a8_gemv_act for one row up to this K
-_OUT_CODES = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32, torch.int32: OUT_I32}
+_OUT_CODES = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32, torch.int32: OUT_I32, SWIGLU: OUT_SWIGLU}
+
+
+def _out_spec(out_dtype, m: int, n: int):
+    """(shape, torch dtype) of a linear output of type out_dtype."""
+    if out_dtype == SWIGLU:
+        if n % 2:
+            raise ValueError("the SwiGLU epilogue needs an even number of output rows")
+        return (m, n // 2), torch.bfloat16
+    return (m, n), out_dtype
 
 # The default 16-level table (ai-toolkit convrot_w4a8_quant.py, FIXED_CODEBOOK):
 # Lloyd-Max levels for a group-normalised Gaussian, index = 4-bit code.
@@ -206,7 +218,8 @@ def _linear_call(fn: str, xq, xs, layer: W4A8Layer, out_dtype, out):
         raise ValueError(f"xq has K={k}, layer has K={layer.in_features}")
     if out_dtype not in _OUT_CODES:
         raise ValueError(f"unsupported out_dtype {out_dtype}")
-    out = _out(out, (m, n), out_dtype, xq.device, "out")
+    shape, dt = _out_spec(out_dtype, m, n)
+    out = _out(out, shape, dt, xq.device, "out")
     bias = layer.bias.data_ptr() if layer.bias is not None else None
     st = getattr(load(), fn)(xq.data_ptr(), xs.data_ptr(), m, layer.qpacked.data_ptr(), layer.srel.data_ptr(),
                              layer.codebook.data_ptr(), layer.s_channel.data_ptr(), bias, n, k, GROUP,
@@ -243,7 +256,8 @@ def w4a8_gemv_act(x: torch.Tensor, layer: W4A8Layer, out_dtype=torch.bfloat16, o
         raise ValueError(f"unsupported out_dtype {out_dtype}")
     if (xq_out is None) != (xs_out is None):
         raise ValueError("xq_out and xs_out go together")
-    out = _out(out, (m, n), out_dtype, x.device, "out")
+    shape, dt = _out_spec(out_dtype, m, n)
+    out = _out(out, shape, dt, x.device, "out")
     if xq_out is not None:
         _out(xq_out, (m, k), torch.int8, x.device, "xq_out")
         _out(xs_out, (m,), torch.float32, x.device, "xs_out")
@@ -273,7 +287,8 @@ def _group_descs(items, out_dtype):
         if mi != m or tuple(xs.shape) != (m,) or k != layer.in_features:
             raise ValueError(f"layer {i}: activations do not match (M must be common to all layers)")
         n = layer.out_features
-        out = _out(out, (m, n), out_dtype, xq.device, "out")
+        shape, dt = _out_spec(out_dtype, m, n)
+        out = _out(out, shape, dt, xq.device, "out")
         outs.append(out)
         arr[i] = GemvLayerDesc(xq.data_ptr(), xs.data_ptr(), layer.qpacked.data_ptr(), layer.srel.data_ptr(),
                                layer.codebook.data_ptr(), layer.s_channel.data_ptr(),
@@ -397,11 +412,12 @@ def linear(x: torch.Tensor, layer: W4A8Layer, out_dtype=torch.bfloat16) -> torch
     shape = x.shape
     x2 = x.reshape(-1, shape[-1]).contiguous()
     if x2.shape[0] == 1 and x2.shape[1] <= FUSED_ACT_MAX_K:
-        return w4a8_gemv_act(x2, layer, out_dtype).reshape(*shape[:-1], layer.out_features)
+        y = w4a8_gemv_act(x2, layer, out_dtype)
+        return y.reshape(*shape[:-1], y.shape[-1])
     xq, xs = rotate_quant_act(x2)
     fn = w4a8_gemv if x2.shape[0] <= GEMV_MAX_M else w4a8_gemm
     y = fn(xq, xs, layer, out_dtype)
-    return y.reshape(*shape[:-1], layer.out_features)
+    return y.reshape(*shape[:-1], y.shape[-1])
 
 
 def prepare(fn: str, *tensors_and_args):
@@ -421,17 +437,19 @@ def prepare(fn: str, *tensors_and_args):
     return run
 
 
-def prepared_linear(fn: str, xq, xs, layer: W4A8Layer, out):
-    """prepare() for w4a8_gemm / w4a8_gemv with the checks of a regular call done once."""
-    _linear_call(fn, xq, xs, layer, out.dtype, out)     # validates shapes and runs once
+def prepared_linear(fn: str, xq, xs, layer: W4A8Layer, out, out_dtype=None):
+    """prepare() for w4a8_gemm / w4a8_gemv with the checks of a regular call done once
+    (out_dtype defaults to out's dtype; pass SWIGLU for the SwiGLU epilogue)."""
+    out_dtype = out.dtype if out_dtype is None else out_dtype
+    _linear_call(fn, xq, xs, layer, out_dtype, out)     # validates shapes and runs once
     bias = layer.bias.data_ptr() if layer.bias is not None else None
     return prepare(fn, xq, xs, xq.shape[0], layer.qpacked, layer.srel, layer.codebook, layer.s_channel, bias,
-                   layer.out_features, layer.in_features, GROUP, _OUT_CODES[out.dtype], out)
+                   layer.out_features, layer.in_features, GROUP, _OUT_CODES[out_dtype], out)
 
 
 def prepared_gemv_act(x, layer: W4A8Layer, out, qmax: int = 127):
     """prepare() for w4a8_gemv_act (no prepared-activation outputs)."""
-    w4a8_gemv_act(x, layer, out.dtype, out, qmax)           # validates shapes and runs once
+    w4a8_gemv_act(x, layer, out.dtype, out, qmax)           # validates shapes and runs once (bf16/f32/i32)
     bias = layer.bias.data_ptr() if layer.bias is not None else None
     return prepare("w4a8_gemv_act", x, x.shape[0], ROT_BLOCK, qmax, layer.qpacked, layer.srel, layer.codebook,
                    layer.s_channel, bias, layer.out_features, layer.in_features, GROUP, _OUT_CODES[out.dtype], out,

@@ -50,7 +50,8 @@ enum w4a8_status {
     W4A8_OK = 0,
     W4A8_ERR_INVALID_ARG = 1,  /* NULL required pointer, negative size, unknown out_type */
     W4A8_ERR_SHAPE = 2,        /* N < 1, K not a positive multiple of 256, K > W4A8_MAX_K,
-                                  N not a multiple of 8 for w4a8_grad_input */
+                                  N not a multiple of 8 for w4a8_grad_input, odd N with
+                                  W4A8_OUT_SWIGLU_BF16 */
     W4A8_ERR_ALIGN = 3,        /* a pointer misses its required alignment */
     W4A8_ERR_UNSUPPORTED = 4,  /* group != 16, rot_block != 256, qmax not in 1..127,
                                   M > W4A8_GEMV_MAX_M for the GEMV entry points,
@@ -59,9 +60,18 @@ enum w4a8_status {
 };
 
 enum w4a8_out_type {
-    W4A8_OUT_BF16 = 0,  /* bfloat16, round to nearest even */
-    W4A8_OUT_F32 = 1,   /* float32 */
-    W4A8_OUT_I32 = 2    /* the raw int32 accumulator acc[m, n], no scaling or bias */
+    W4A8_OUT_BF16 = 0,        /* bfloat16, round to nearest even */
+    W4A8_OUT_F32 = 1,         /* float32 */
+    W4A8_OUT_I32 = 2,         /* the raw int32 accumulator acc[m, n], no scaling or bias */
+    W4A8_OUT_SWIGLU_BF16 = 3  /* SwiGLU fused into the epilogue (h3-rs src/weights.rs,
+                                 swiglu_interleaved): the layer's rows hold gate and up
+                                 projections interleaved (gate j in row 2j, up j in row
+                                 2j + 1, as interleave_rows/interleave_swiglu lay them out;
+                                 quantisation is row-wise, so the rows may be interleaved
+                                 before or after it); out is bf16 [M, N/2] with
+                                 out[m, j] = bf16(silu(y[m, 2j]) * y[m, 2j + 1]), y the fp32
+                                 epilogue value and silu(g) = g / (1 + exp(-g)) in fp32.
+                                 N must be even. */
 };
 
 #define W4A8_ROT_BLOCK 256
@@ -114,8 +124,8 @@ int decode_w4_to_int8(const uint8_t* qpacked, const uint8_t* srel, const float* 
  *   codebook, s_channel
  *   bias                in   float [N] or NULL
  *   N, K, group              sizes; group must be 16
- *   out_type                 W4A8_OUT_BF16, W4A8_OUT_F32 or W4A8_OUT_I32
- *   out                 out  [M, N] of the chosen type
+ *   out_type                 W4A8_OUT_BF16, W4A8_OUT_F32, W4A8_OUT_I32 or W4A8_OUT_SWIGLU_BF16
+ *   out                 out  [M, N] of the chosen type ([M, N/2] bf16 for SwiGLU)
  */
 int w4a8_gemm(const int8_t* xq, const float* xs, int64_t M,
               const uint8_t* qpacked, const uint8_t* srel, const float* codebook,

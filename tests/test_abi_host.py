@@ -46,7 +46,7 @@ def test_status_strings(w4a8):
         "W4A8_OK", "W4A8_ERR_INVALID_ARG", "W4A8_ERR_SHAPE", "W4A8_ERR_ALIGN", "W4A8_ERR_UNSUPPORTED",
         "W4A8_ERR_HIP"]
     assert w4a8.status_string(99) == "W4A8_ERR_UNKNOWN"
-    assert w4a8.load().w4a8_abi_version() == w4a8.ABI_VERSION == 6
+    assert w4a8.load().w4a8_abi_version() == w4a8.ABI_VERSION == 7
 
 
 A = 1 << 20          # a 16-byte-aligned fake address (never dereferenced: validation fails first)
@@ -69,7 +69,9 @@ def test_linear_validation(w4a8, fn):
         assert _lin(w4a8, fn, K=k) == w4a8.ERR_SHAPE, k
     assert _lin(w4a8, fn, K=-256) == w4a8.ERR_INVALID_ARG
     assert _lin(w4a8, fn, group=32) == w4a8.ERR_UNSUPPORTED
-    assert _lin(w4a8, fn, out_type=3) == w4a8.ERR_INVALID_ARG
+    assert _lin(w4a8, fn, out_type=4) == w4a8.ERR_INVALID_ARG
+    assert _lin(w4a8, fn, out_type=3, N=63) == w4a8.ERR_SHAPE          # SwiGLU pairs rows
+    assert _lin(w4a8, fn, out_type=3, M=0) == w4a8.OK
     for p in ("qp", "srel", "cb", "sch"):
         assert _lin(w4a8, fn, **{p: None}) == w4a8.ERR_INVALID_ARG, p
     for p in ("xq", "xs", "out"):
@@ -108,7 +110,8 @@ def test_gemv_act_validation(w4a8):
     assert _act(w4a8, qmax=0) == w4a8.ERR_UNSUPPORTED
     assert _act(w4a8, qmax=128) == w4a8.ERR_UNSUPPORTED
     assert _act(w4a8, group=32) == w4a8.ERR_UNSUPPORTED
-    assert _act(w4a8, out_type=3) == w4a8.ERR_INVALID_ARG
+    assert _act(w4a8, out_type=4) == w4a8.ERR_INVALID_ARG
+    assert _act(w4a8, out_type=3, N=63) == w4a8.ERR_SHAPE
     for p in ("x", "out", "qp", "srel", "cb", "sch"):
         assert _act(w4a8, **{p: None}) == w4a8.ERR_INVALID_ARG, p
     assert _act(w4a8, xq_out=A) == w4a8.ERR_INVALID_ARG                # one of the pair
