@@ -14,6 +14,11 @@
 //                        fp32(w_rot / s_channel) times s_channel (fp32).
 //   dequantize        -- dequantize_w4a8: fp32(w8 * s_channel), rotated back to the plain
 //                        basis (the fp64 block sum of these terms is exact; rounded once).
+//   lora_merge        -- h3-rs src/weights.rs QLinear::merge_loras for this format: the
+//                        dequantised plain-basis weight plus one adapter's delta
+//                        fp32(scale * sum_r B[n, r] * A[r, k]) (fp64 products and sums in
+//                        r order, no fused multiply-add), added in fp32; the result goes
+//                        back through quantize_w4.
 //
 // Layout: a block of 256 threads covers one 4096-column chunk of one row (grid =
 // rows x chunks); thread t holds the 16 columns of group t of the chunk, which is the
@@ -154,7 +159,64 @@ __global__ __launch_bounds__(RG_THREADS) void dequant_kernel(const uint8_t* __re
     if (ok) store16(out + row * K + col, w);
 }
 
+// The dequantised, rotated-back weight plus a low-rank delta (one block per row chunk).
+__global__ __launch_bounds__(RG_THREADS) void lora_merge_kernel(const uint8_t* __restrict__ qpacked,
+                                                                const uint8_t* __restrict__ srel,
+                                                                const float* __restrict__ codebook,
+                                                                const float* __restrict__ s_channel, int K,
+                                                                int nchunk, const float* __restrict__ lora_a,
+                                                                const float* __restrict__ lora_b, int rank,
+                                                                float scale, float* __restrict__ out) {
+    __shared__ double tbuf[16 * 16 * QTSTRIDE];
+    __shared__ float fbuf[16 * (256 + 16)];
+    const int tid = threadIdx.x, slot = tid >> 4, l16 = tid & 15;
+    const int64_t row = blockIdx.x / nchunk;
+    const int c0 = (blockIdx.x - (int)(row * nchunk)) * RG_CHUNK;
+    const int col = c0 + tid * 16;
+    const bool ok = col < K;
+    float w[16];
+    if (ok) {
+        const float s = e4m3fn_to_f32(srel[row * (K >> 4) + (col >> 4)]);
+        const float sch = s_channel[row];
+        const uint2 q = *reinterpret_cast<const uint2*>(qpacked + row * (K >> 1) + (col >> 1));
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const uint32_t code = ((k < 8 ? q.x : q.y) >> (4 * (k & 7))) & 15u;
+            w[k] = __fmul_rn((float)(int8_t)(uint8_t)grid_level(codebook[code], s), sch);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) w[k] = 0.0f;
+    }
+    rotate16_in_place(w, slot, l16, tbuf, fbuf);   // block-uniform: back to the plain basis
+    if (!ok) return;
+    double d[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) d[k] = 0.0;
+    for (int r = 0; r < rank; ++r) {
+        const double b = (double)lora_b[row * rank + r];
+        float a[16];
+        load16(lora_a + (int64_t)r * K + col, a);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) d[k] = __dadd_rn(d[k], __dmul_rn(b, (double)a[k]));
+    }
+    const double sc = (double)scale;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) w[k] = __fadd_rn(w[k], (float)__dmul_rn(d[k], sc));
+    store16(out + row * K + col, w);
+}
+
 }  // namespace
+
+hipError_t launch_lora_merge(const uint8_t* qpacked, const uint8_t* srel, const float* codebook,
+                             const float* s_channel, int64_t N, int K, const float* lora_a, const float* lora_b,
+                             int rank, float scale, float* out, hipStream_t stream) {
+    (void)hipGetLastError();
+    const int nchunk = (K + RG_CHUNK - 1) / RG_CHUNK;
+    hipLaunchKernelGGL(lora_merge_kernel, dim3((unsigned)(N * nchunk)), dim3(RG_THREADS), 0, stream, qpacked, srel,
+                       codebook, s_channel, K, nchunk, lora_a, lora_b, rank, scale, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_requantize(const float* w, int64_t N, int K, int rotated, const float* codebook,
                              const uint8_t* srel, const float* s_channel, const float* u, uint8_t* qpacked,

@@ -31,6 +31,9 @@ hipError_t launch_fake_quant(const float* w_rot, int64_t N, int K, const float* 
                              const float* s_channel, float* out, hipStream_t stream);
 hipError_t launch_grad_input(const uint16_t* grad, int M, int N, int K, const uint8_t* qp, const uint8_t* srel,
                              const float* codebook, const float* s_channel, uint16_t* out, hipStream_t stream);
+hipError_t launch_lora_merge(const uint8_t* qpacked, const uint8_t* srel, const float* codebook,
+                             const float* s_channel, int64_t N, int K, const float* lora_a, const float* lora_b,
+                             int rank, float scale, float* out, hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t* qpacked, const uint8_t* srel, const float* codebook,
                              const float* s_channel, int64_t N, int K, int rotate_back, float* out,
                              hipStream_t stream);
@@ -269,6 +272,25 @@ int w4a8_grad_input(const void* grad, int64_t M, const uint8_t* qpacked, const u
                                             static_cast<hipStream_t>(stream)));
 }
 
+int lora_merge_w4(const uint8_t* qpacked, const uint8_t* srel, const float* codebook, const float* s_channel,
+                  int64_t N, int64_t K, int32_t rot_block, int32_t group, const float* lora_a, const float* lora_b,
+                  int32_t rank, float scale, float* out, void* stream) {
+    int st = check_n(N);
+    if (st) return st;
+    if ((st = check_k(K))) return st;
+    if ((st = check_row_chunks(N, K))) return st;
+    if (rot_block != W4A8_ROT_BLOCK || group != W4A8_GROUP) return W4A8_ERR_UNSUPPORTED;
+    if (rank < 0) return W4A8_ERR_INVALID_ARG;
+    if (rank > W4A8_MAX_LORA_RANK) return W4A8_ERR_UNSUPPORTED;
+    if (!qpacked || !srel || !codebook || !s_channel || !out) return W4A8_ERR_INVALID_ARG;
+    if (rank > 0 && (!lora_a || !lora_b)) return W4A8_ERR_INVALID_ARG;
+    if (!aligned(qpacked, 16) || !aligned(srel, 16) || !aligned(codebook, 4) || !aligned(s_channel, 4) ||
+        !aligned(out, 16) || !aligned(lora_a, 16) || !aligned(lora_b, 4))
+        return W4A8_ERR_ALIGN;
+    return launched(w4a8::launch_lora_merge(qpacked, srel, codebook, s_channel, N, (int)K, lora_a, lora_b, rank,
+                                            scale, out, static_cast<hipStream_t>(stream)));
+}
+
 const char* w4a8_status_string(int status) {
     switch (status) {
         case W4A8_OK: return "W4A8_OK";
@@ -281,6 +303,6 @@ const char* w4a8_status_string(int status) {
     }
 }
 
-int w4a8_abi_version(void) { return 7; }
+int w4a8_abi_version(void) { return 8; }
 
 }  // extern "C"

@@ -26,7 +26,7 @@ OUT_BF16, OUT_F32, OUT_I32, OUT_SWIGLU = 0, 1, 2, 3
 # gate/up-interleaved rows
 SWIGLU = "swiglu"
 ROT_BLOCK, GROUP, GEMV_MAX_M, MAX_K = 256, 16, 8, 131072
-ABI_VERSION = 7
+ABI_VERSION = 8
 FUSED_ACT_MAX_K = 4096   # linear() uses w4a8_gemv_act for one row up to this K
 _OUT_CODES = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32, torch.int32: OUT_I32, SWIGLU: OUT_SWIGLU}
 
@@ -63,6 +63,7 @@ SIGNATURES = {
     "fake_quant_w4": [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P],
     "dequantize_w4": [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P],
     "w4a8_grad_input": [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I32, _P, _P],
+    "lora_merge_w4": [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _I32, ctypes.c_float, _P, _P],
     "w4a8_status_string": [ctypes.c_int],
     "w4a8_abi_version": [],
 }
@@ -402,6 +403,35 @@ def grad_input(grad: torch.Tensor, layer: W4A8Layer, out: torch.Tensor = None) -
                                                      layer.s_channel.data_ptr(), n, layer.in_features, GROUP,
                                                      out.data_ptr(), _stream(grad)))
     return out
+
+
+def lora_merged_weight(layer: W4A8Layer, lora_a: torch.Tensor, lora_b: torch.Tensor, scale: float,
+                       out: torch.Tensor = None) -> torch.Tensor:
+    """The layer's plain-basis fp32 weight [N, K] with one adapter folded in:
+    dequantised weight + scale * (lora_b [N, r] @ lora_a [r, K])."""
+    layer.check()
+    n, k = layer.out_features, layer.in_features
+    _dev(lora_a, torch.float32, "lora_a")
+    _dev(lora_b, torch.float32, "lora_b")
+    r = lora_a.shape[0]
+    if tuple(lora_a.shape) != (r, k) or tuple(lora_b.shape) != (n, r):
+        raise ValueError(f"adapter shapes {tuple(lora_a.shape)}, {tuple(lora_b.shape)} do not fit {n}x{k}")
+    out = _out(out, (n, k), torch.float32, layer.qpacked.device, "out")
+    _check("lora_merge_w4", load().lora_merge_w4(layer.qpacked.data_ptr(), layer.srel.data_ptr(),
+                                                 layer.codebook.data_ptr(), layer.s_channel.data_ptr(), n, k,
+                                                 ROT_BLOCK, GROUP, lora_a.data_ptr() if r else None,
+                                                 lora_b.data_ptr() if r else None, r, float(scale), out.data_ptr(),
+                                                 _stream(layer.qpacked)))
+    return out
+
+
+def merge_lora(layer: W4A8Layer, lora_a: torch.Tensor, lora_b: torch.Tensor, scale: float) -> W4A8Layer:
+    """A new layer with the adapter folded in (dequantise, add, requantise with the
+    layer's codebook); the bias is kept."""
+    w = lora_merged_weight(layer, lora_a, lora_b, scale)
+    merged = quantize_w4(w, codebook=layer.codebook, bias=layer.bias)
+    del w
+    return merged
 
 
 def linear(x: torch.Tensor, layer: W4A8Layer, out_dtype=torch.bfloat16) -> torch.Tensor:

@@ -78,6 +78,7 @@ enum w4a8_out_type {
 #define W4A8_GROUP 16
 #define W4A8_GEMV_MAX_M 8
 #define W4A8_MAX_K 131072
+#define W4A8_MAX_LORA_RANK 4096
 
 /*
  * rotate_quant_act -- steps 1 and 2 for M rows of activations.
@@ -312,6 +313,29 @@ int dequantize_w4(const uint8_t* qpacked, const uint8_t* srel, const float* code
 int w4a8_grad_input(const void* grad, int64_t M, const uint8_t* qpacked, const uint8_t* srel,
                     const float* codebook, const float* s_channel, int64_t N, int64_t K, int32_t group,
                     void* out, void* stream);
+
+/*
+ * lora_merge_w4 -- folds one low-rank adapter into the layer's weight (h3-rs 0.2.0
+ * src/weights.rs, QLinear::merge_loras: dequantise, add the delta, requantise), the
+ * first two steps:
+ *   out[n, k] = fp32(w[n, k] + fp32(scale * sum_r lora_b[n, r] * lora_a[r, k]))
+ * with w the dequantised weight in the plain basis (as dequantize_w4 with rotate_back)
+ * and the sum over r formed in fp64 in r order (each product, then each sum, rounded
+ * in fp64; no fused multiply-add), times scale in fp64, rounded once to fp32.  The
+ * result is the plain-basis fp32 weight that quantize_w4 (or requantize_codes_w4) turns
+ * back into the layer; several adapters are merged one call at a time.
+ *
+ *   qpacked, srel, codebook, s_channel   in   the layer storage
+ *   N, K, rot_block, group                    sizes; rot_block 256, group 16
+ *   lora_a                               in   float [rank, K] (the down projection A)
+ *   lora_b                               in   float [N, rank] (the up projection B)
+ *   rank                                      0..W4A8_MAX_LORA_RANK (0: out is the dequantised weight)
+ *   scale                                     the adapter's scale (alpha / rank, say)
+ *   out                                  out  float [N, K]
+ */
+int lora_merge_w4(const uint8_t* qpacked, const uint8_t* srel, const float* codebook, const float* s_channel,
+                  int64_t N, int64_t K, int32_t rot_block, int32_t group, const float* lora_a, const float* lora_b,
+                  int32_t rank, float scale, float* out, void* stream);
 
 /* Name of a status code ("W4A8_OK", ...); never NULL. */
 const char* w4a8_status_string(int status);

@@ -29,9 +29,9 @@ def test_header_declares_the_operations():
     names = _declared_functions()
     for n in ("rotate_quant_act", "decode_w4_to_int8", "w4a8_gemm", "w4a8_gemv", "w4a8_gemv_grouped",
               "quantize_w4", "w4a8_gemv_act", "w4a8_gemv_act_max_k", "requantize_codes_w4", "fake_quant_w4",
-              "dequantize_w4", "w4a8_grad_input", "w4a8_status_string", "w4a8_abi_version"):
+              "dequantize_w4", "w4a8_grad_input", "lora_merge_w4", "w4a8_status_string", "w4a8_abi_version"):
         assert n in names
-    assert len(names) == 14, names
+    assert len(names) == 15, names
 
 
 def test_library_exports_every_declared_symbol(w4a8):
@@ -46,7 +46,7 @@ def test_status_strings(w4a8):
         "W4A8_OK", "W4A8_ERR_INVALID_ARG", "W4A8_ERR_SHAPE", "W4A8_ERR_ALIGN", "W4A8_ERR_UNSUPPORTED",
         "W4A8_ERR_HIP"]
     assert w4a8.status_string(99) == "W4A8_ERR_UNKNOWN"
-    assert w4a8.load().w4a8_abi_version() == w4a8.ABI_VERSION == 7
+    assert w4a8.load().w4a8_abi_version() == w4a8.ABI_VERSION == 8
 
 
 A = 1 << 20          # a 16-byte-aligned fake address (never dereferenced: validation fails first)
@@ -174,6 +174,23 @@ def test_grad_input_validation(w4a8):
     for p in ("g", "out", "qp", "srel"):
         assert gi(**{p: A + 8}) == w4a8.ERR_ALIGN, p
     assert gi(M=0, g=None, out=None, qp=U) == w4a8.ERR_ALIGN
+
+
+def test_lora_merge_validation(w4a8):
+    def lm(**kw):
+        a = dict(qp=A, srel=A, cb=A, sch=A, N=8, K=256, rot=256, group=16, la=A, lb=A, r=4, scale=0.5, out=A)
+        a.update(kw)
+        return w4a8.call("lora_merge_w4", a["qp"], a["srel"], a["cb"], a["sch"], a["N"], a["K"], a["rot"], a["group"],
+                         a["la"], a["lb"], a["r"], a["scale"], a["out"], None)
+
+    assert lm(r=-1) == w4a8.ERR_INVALID_ARG
+    assert lm(r=4097) == w4a8.ERR_UNSUPPORTED
+    assert lm(la=None) == w4a8.ERR_INVALID_ARG and lm(lb=None) == w4a8.ERR_INVALID_ARG
+    assert lm(r=0, la=None, lb=None, out=A + 8) == w4a8.ERR_ALIGN       # rank 0 needs no adapter
+    assert lm(la=A + 4) == w4a8.ERR_ALIGN and lm(lb=A + 2) == w4a8.ERR_ALIGN
+    assert lm(K=300) == w4a8.ERR_SHAPE and lm(N=0) == w4a8.ERR_SHAPE
+    assert lm(rot=128) == w4a8.ERR_UNSUPPORTED and lm(group=8) == w4a8.ERR_UNSUPPORTED
+    assert lm(qp=None) == w4a8.ERR_INVALID_ARG
 
 
 def test_rotate_quant_validation(w4a8):
