@@ -29,6 +29,7 @@ import numpy as np
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA, TOPS
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "W4A8 linear TOPS (M=2048) and GEMV weight GB/s (M=1..8), % of roofline"
 
 
@@ -48,6 +49,7 @@ def parse():
                    help="GPU spin before a launch batch, so the host can queue the whole batch")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-gemv", action="store_true")
+    p.add_argument("--no-training", action="store_true", help="skip the training-path and variant kernels")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device-to-device copy 5 times (counter calibration)")
     return p.parse_args()
@@ -231,6 +233,77 @@ def bench_decode_set(args, torch, B, device):
             "grouped_frac": round(wbytes / (grp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
+def time_us(torch, call, reps, sleep_cycles):
+    """Mean GPU time of one call over `reps` back-to-back launches queued behind a GPU
+    sleep (events around the whole run)."""
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(sleep_cycles)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def bench_training(args, torch, B, device):
+    """The training-path and variant kernels on the 4096 x 4096 layer: the
+    straight-through backward at M = 2048, code-only requantisation (nearest and
+    stochastic), fake quantisation, dequantisation, a rank-64 LoRA merge, and the
+    SwiGLU epilogue of the prefill GEMM."""
+    from bit_codebook_quantized_amd import synth
+    M, N, K = 2048, 4096, 4096
+    sleep = int(args.sleep_cycles) // 4
+    w = synth.gaussian_weight_device(N, K, seed=synth.seed_for(5, 0, synth.ROLE_WEIGHT), device=device)
+    layer = B.quantize_w4(w)
+    gen = torch.Generator(device).manual_seed(5)
+    w2 = w + torch.randn(N, K, device=device, generator=gen) * 0.004
+    u = torch.rand(N, K, device=device, generator=gen)
+    grad = torch.randn(M, N, device=device, generator=gen).to(torch.bfloat16)
+    gx = torch.empty(M, K, dtype=torch.bfloat16, device=device)
+    codes = torch.empty(N, K // 2, dtype=torch.uint8, device=device)
+    f32 = torch.empty(N, K, dtype=torch.float32, device=device)
+    la = torch.randn(64, K, device=device, generator=gen) * 0.02
+    lb = torch.randn(N, 64, device=device, generator=gen) * 0.02
+    x = torch.from_numpy(synth.activations(M, K, seed=synth.seed_for(5, 0, synth.ROLE_ACT))).to(
+        torch.bfloat16).to(device)
+    xq, xs = B.rotate_quant_act(x)
+    y_sw = torch.empty(M, N // 2, dtype=torch.bfloat16, device=device)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=device)
+    calls = {
+        "grad_input": B.prepare("w4a8_grad_input", grad, M, layer.qpacked, layer.srel, layer.codebook,
+                                layer.s_channel, N, K, 16, gx),
+        "requantize_nearest": lambda: B.requantize_codes(w2, layer, out=codes),
+        "requantize_stochastic": lambda: B.requantize_codes(w2, layer, u=u, out=codes),
+        "fake_quant": lambda: B.fake_quant(w2, layer, out=f32),
+        "dequantize": lambda: B.dequantize(layer, out=f32),
+        "lora_merge_r64": lambda: B.lora_merged_weight(layer, la, lb, 0.5, out=f32),
+        "gemm_swiglu": B.prepared_linear("w4a8_gemm", xq, xs, layer, y_sw, B.SWIGLU),
+        "gemm_plain": B.prepared_linear("w4a8_gemm", xq, xs, layer, y),
+    }
+    us = {k: time_us(torch, c, 10, sleep) for k, c in calls.items()}
+    wb = weight_bytes(N, K)
+    fp = N * K * 4
+    res = {
+        "layer": "4096 x 4096",
+        "grad_input": {"M": M, "us": round(us["grad_input"], 1),
+                       "TFLOPs": round(2 * M * N * K / us["grad_input"] / 1e6, 1),
+                       "frac_bf16_peak": round(2 * M * N * K / us["grad_input"] / 1e6 / BF16_PEAK_TFLOPS, 4)},
+    }
+    for name, nbytes in [("requantize_nearest", fp + N * K // 2 + N * K // 16),
+                         ("requantize_stochastic", 2 * fp + N * K // 2 + N * K // 16),
+                         ("fake_quant", 2 * fp + N * K // 16),
+                         ("dequantize", wb + fp),
+                         ("lora_merge_r64", wb + fp + 2 * 64 * N * 4)]:
+        res[name] = {"us": round(us[name], 1), "GBps": round(nbytes / (us[name] * 1e-6) / 1e9, 1),
+                     "frac_hbm": round(nbytes / (us[name] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    res["gemm_swiglu_epilogue"] = {"M": M, "us": round(us["gemm_swiglu"], 2),
+                                   "plain_gemm_us": round(us["gemm_plain"], 2)}
+    return res
+
+
 def cpu_baseline(pre, min_seconds=10.0):
     """The oracle, untuned, on the host cores: the whole M=2048 layer step (rotate +
     quantise, decode, exact contraction, epilogue), repeated until at least
@@ -309,6 +382,7 @@ def main():
     pre = bench_prefill(args, torch, B, device)
     gemv = None if args.no_gemv else bench_gemv(args, torch, B, device)
     decode_set = None if args.no_gemv else bench_decode_set(args, torch, B, device)
+    training = None if args.no_training else bench_training(args, torch, B, device)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre)
 
     tops = pre["ops"] / pre["wall_s"] / 1e12
@@ -341,6 +415,7 @@ def main():
                              "frac_hbm": round(pre["rq_bytes"] / (pre["rq_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "gemv": gemv,
         "gemv_decode_set": decode_set,
+        "training_and_variants": training,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

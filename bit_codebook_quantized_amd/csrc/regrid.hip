@@ -95,7 +95,7 @@ __global__ __launch_bounds__(RG_THREADS) void requant_kernel(const float* __rest
             code = stochastic16(t, r[k], lvl);
         } else {
             float dummy;
-            code = (uint32_t)nearest16(t, lvl, &dummy);
+            code = (uint32_t)nearest16_any(t, lvl, &dummy);
         }
         packed[k >> 3] |= code << (4 * (k & 7));
     }
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(RG_THREADS) void fake_quant_kernel(const float* __r
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         float lv;
-        (void)nearest16(__fdiv_rn(w[k], sch), lvl, &lv);
+        (void)nearest16_any(__fdiv_rn(w[k], sch), lvl, &lv);
         y[k] = __fmul_rn(lv, sch);
     }
     store16(out + g * 16, y);

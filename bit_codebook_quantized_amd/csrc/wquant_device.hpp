@@ -43,10 +43,32 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn(float x) {
 
 // Nearest of 16 levels ([AT] _assign_codes / _assign_grid): p = count of levels < x
 // (the left insertion point for non-decreasing levels), candidates at indices p - 1 and
-// p clamped to 0..15, the upper one only if strictly closer (fp32 distances).  The
-// candidates are taken by index, so the rule is the page's for any level order.
+// p clamped to 0..15, the upper one only if strictly closer (fp32 distances).
 // Returns the code; *lv receives the chosen level.
+//
+// nearest16 is for non-decreasing levels (a sorted codebook and a positive scale, as
+// in the quantiser): the candidates are then the last level below x and the first one
+// not below it, tracked in the same pass as the count.  nearest16_any takes the two
+// candidates by index, so it follows the rule for levels in any order (stored scale
+// bytes of either sign); for non-decreasing levels the two agree.
 __device__ __forceinline__ int nearest16(float x, const float (&lvl)[16], float* lv) {
+    int p = 0;
+    float lo = lvl[0], hi = lvl[15];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        if (lvl[c] < x) { ++p; lo = lvl[c]; }
+    }
+#pragma unroll
+    for (int c = 15; c >= 0; --c)
+        if (!(lvl[c] < x)) hi = lvl[c];
+    const int ilo = p > 0 ? p - 1 : 0, ihi = p < 15 ? p : 15;
+    const float dlo = __builtin_fabsf(__fsub_rn(x, lo)), dhi = __builtin_fabsf(__fsub_rn(x, hi));
+    const bool up = dhi < dlo;
+    *lv = up ? hi : lo;
+    return up ? ihi : ilo;
+}
+
+__device__ __forceinline__ int nearest16_any(float x, const float (&lvl)[16], float* lv) {
     int p = 0;
 #pragma unroll
     for (int c = 0; c < 16; ++c) p += lvl[c] < x ? 1 : 0;
