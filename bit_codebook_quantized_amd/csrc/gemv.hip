@@ -43,27 +43,33 @@ constexpr int log2i(int v) { return v <= 1 ? 0 : 1 + log2i(v / 2); }
 // Columns of activations held in LDS at a time.
 __host__ __device__ constexpr int slab_cols(int mm) { return mm == 1 ? 32768 : mm == 2 ? 16384 : mm <= 4 ? 8192 : 4096; }
 
+// A batch: lane l takes the 4 consecutive groups 4l .. 4l + 3 of the batch's 256 (64
+// columns) of each of its R rows: 32 bytes of codes (two 16-byte loads) and the 4 scale
+// bytes (one dword), three wide loads per row.
 template <int R>
 struct Batch {
-    uint2 q[GV_BATCH][R];
-    uint32_t s[GV_BATCH][R];
+    uint4 q[2][R];
+    uint32_t s[R];
 };
 
-// Loads are unconditional (slots past the row end re-read its last group), so the
+// Loads are unconditional (lanes past the row end re-read its last 4 groups), so the
 // compiler can count the loads in flight and wait for exactly the batch it needs.
 template <int R>
 __device__ __forceinline__ void load_batch(Batch<R>& b, const uint8_t* const (&qrow)[R], const uint8_t* const (&srow)[R],
                                            int jbase, int nchunk) {
+    const int j = min(jbase, nchunk - 4);   // nchunk is a multiple of 16
 #pragma unroll
-    for (int u = 0; u < GV_BATCH; ++u) {
-        const int j = min(jbase + 64 * u, nchunk - 1);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            b.q[u][r] = *reinterpret_cast<const uint2*>(qrow[r] + (int64_t)j * 8);
-            b.s[u][r] = srow[r][j];
-        }
+    for (int r = 0; r < R; ++r) {
+        b.q[0][r] = *reinterpret_cast<const uint4*>(qrow[r] + (int64_t)j * 8);
+        b.q[1][r] = *reinterpret_cast<const uint4*>(qrow[r] + (int64_t)j * 8 + 16);
+        b.s[r] = *reinterpret_cast<const uint32_t*>(srow[r] + j);
     }
 }
+
+// Position of 16-byte chunk c of an activation slab in LDS: the two low bits are XORed
+// with bits 4-5, so the 16 lanes of a read (chunks 4l + u, l = 0..15) hit 16 different
+// bank groups.
+__device__ __forceinline__ int act_chunk(int c) { return c ^ ((c >> 4) & 3); }
 
 // Activation staging: MM rows x cols bytes of xq from column k0 (cols <= slab_cols(MM))
 // -> act[m * slab_cols(MM) ...].  Every load is issued before the first wait; `between`
@@ -88,7 +94,7 @@ __device__ __forceinline__ void stage_acts_n(uint8_t* act, const int8_t* __restr
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int i = min((int)threadIdx.x + 256 * c, per_row - 1);
-            *reinterpret_cast<uint4*>(act + m * slab_cols(MM) + i * 16) = v[m][c];
+            *reinterpret_cast<uint4*>(act + m * slab_cols(MM) + act_chunk(i) * 16) = v[m][c];
         }
 }
 
@@ -188,7 +194,8 @@ __device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds,
         }
         if ((nch == 1 || !pass1) && ok) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) act[row * SLAB + blk * 256 + 16 * i + l16] = (uint8_t)quant1(r[i], inv, qmaxf);
+            for (int i = 0; i < 16; ++i)
+                act[row * SLAB + act_chunk(16 * blk + i) * 16 + l16] = (uint8_t)quant1(r[i], inv, qmaxf);
         }
     };
 
@@ -219,7 +226,7 @@ __device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds,
         for (int i = tid; i < MM * per_row; i += GV_THREADS) {
             const int m = i / per_row, c = i - m * per_row;
             *reinterpret_cast<uint4*>(xq_out + (int64_t)m * K + c * 16) =
-                *reinterpret_cast<const uint4*>(act + m * SLAB + c * 16);
+                *reinterpret_cast<const uint4*>(act + m * SLAB + act_chunk(c) * 16);
         }
     }
 }
@@ -260,7 +267,7 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
             qr[r] = qp + (int64_t)n * KH;
             sr[r] = srel + (int64_t)n * G;
         }
-        load_batch<R>(dst, qr, sr, lane + gb * 64 * GV_BATCH, nchunk);
+        load_batch<R>(dst, qr, sr, 4 * lane + gb * 64 * GV_BATCH, nchunk);
     };
 
     float* xs_w = reinterpret_cast<float*>(act + MM * SLAB);   // the rows' activation scales
@@ -322,18 +329,19 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
                 __syncthreads();
             }
         }
+        const int jb = 4 * lane + gb * 64 * GV_BATCH;   // the lane's first group of the batch
+        if (jb < nchunk) {                                // all 4 groups, or none (nchunk % 16 == 0)
 #pragma unroll
-        for (int u = 0; u < GV_BATCH; ++u) {
-            const int j = lane + (gb * GV_BATCH + u) * 64;
-            if (j < nchunk) {
+            for (int u = 0; u < GV_BATCH; ++u) {
+                const int ca = act_chunk(jb + u - (slab_k0 >> 4));
                 uint4 a[MM];
 #pragma unroll
-                for (int m = 0; m < MM; ++m)
-                    a[m] = *reinterpret_cast<const uint4*>(act + m * SLAB + (j * 16 - slab_k0));
+                for (int m = 0; m < MM; ++m) a[m] = *reinterpret_cast<const uint4*>(act + m * SLAB + ca * 16);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const uint4 tt = lut4[cur.s[u][r]];
-                    const uint2 d0 = decode8(cur.q[u][r].x, tt), d1 = decode8(cur.q[u][r].y, tt);
+                    const uint4 tt = lut4[(cur.s[r] >> (8 * u)) & 0xFFu];
+                    const uint4 qq = cur.q[u >> 1][r];
+                    const uint2 d0 = decode8((u & 1) ? qq.z : qq.x, tt), d1 = decode8((u & 1) ? qq.w : qq.y, tt);
 #pragma unroll
                     for (int m = 0; m < MM; ++m) {
                         int32_t sacc = acc[r * MM + m];
