@@ -477,12 +477,14 @@ def prepared_linear(fn: str, xq, xs, layer: W4A8Layer, out, out_dtype=None):
                    layer.out_features, layer.in_features, GROUP, _OUT_CODES[out_dtype], out)
 
 
-def prepared_gemv_act(x, layer: W4A8Layer, out, qmax: int = 127):
-    """prepare() for w4a8_gemv_act (no prepared-activation outputs)."""
-    w4a8_gemv_act(x, layer, out.dtype, out, qmax)           # validates shapes and runs once (bf16/f32/i32)
+def prepared_gemv_act(x, layer: W4A8Layer, out, qmax: int = 127, out_dtype=None):
+    """prepare() for w4a8_gemv_act (no prepared-activation outputs); out_dtype defaults
+    to out's dtype (pass SWIGLU for the SwiGLU epilogue)."""
+    out_dtype = out.dtype if out_dtype is None else out_dtype
+    w4a8_gemv_act(x, layer, out_dtype, out, qmax)           # validates shapes and runs once
     bias = layer.bias.data_ptr() if layer.bias is not None else None
     return prepare("w4a8_gemv_act", x, x.shape[0], ROT_BLOCK, qmax, layer.qpacked, layer.srel, layer.codebook,
-                   layer.s_channel, bias, layer.out_features, layer.in_features, GROUP, _OUT_CODES[out.dtype], out,
+                   layer.s_channel, bias, layer.out_features, layer.in_features, GROUP, _OUT_CODES[out_dtype], out,
                    None, None)
 
 

@@ -110,6 +110,23 @@ def test_swiglu_mlp_up_projection_full_size_sampled_rows():
     check(y[torch.from_numpy(rows).to(DEV)], reference(xq, xs, host, rows), "C3 up sampled")
 
 
+def test_swiglu_prepared_calls():
+    layer, _ = gate_up_layer(64, 512, synth.seed_for(19, 200, 0), with_bias=True)
+    x = torch.from_numpy(synth.activations(1, 512, seed=synth.seed_for(19, 200, 1))).to(torch.bfloat16).to(DEV)
+    xq, xs = B.rotate_quant_act(x)
+    ref = B.w4a8_gemv(xq, xs, layer, B.SWIGLU)
+    out_a = torch.empty(1, 64, dtype=torch.bfloat16, device=DEV)
+    run_a = B.prepared_gemv_act(x, layer, out_a, out_dtype=B.SWIGLU)
+    out_l = torch.empty(1, 64, dtype=torch.bfloat16, device=DEV)
+    run_l = B.prepared_linear("w4a8_gemv", xq, xs, layer, out_l, B.SWIGLU)
+    out_a.zero_()
+    out_l.zero_()
+    run_a()
+    run_l()
+    assert torch.equal(out_a.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(out_l.view(torch.int16), ref.view(torch.int16))
+
+
 def test_swiglu_rejects_odd_rows():
     packed, srel, sch = synth.random_layer_bytes(63, 256, seed=3)
     layer = B.W4A8Layer.from_host(packed, srel, O.FIXED_CODEBOOK, sch, None, device=DEV)
