@@ -250,3 +250,25 @@ def test_streams_are_respected():
         y = B.linear(xd, layer)
     s.synchronize()
     assert np.array_equal(bf16_bits(y), ref)
+
+
+def test_accumulator_extremes_at_the_largest_k():
+    # K = 131072, every activation +127 or -127 and every weight -128 (uniform codebook
+    # code 0 = -8 at scale 16): |acc| = 127 * 128 * 131072 = 2 130 706 432, the largest the
+    # ABI allows, just inside int32; the raw accumulator must be exact on both paths
+    k, n = 131072, 24
+    packed = np.zeros((n, k // 2), np.uint8)             # code 0 in both nibbles
+    srel = np.full((n, k // 16), 0x58, np.uint8)         # e4m3 0x58 = 16.0
+    sch = np.full(n, 1e-6, np.float32)
+    cb = O.uniform_codebook()
+    layer = host_layer(packed, srel, sch, cb)
+    for m, fn in [(3, B.w4a8_gemv), (9, B.w4a8_gemm)]:
+        xq_np = np.full((m, k), 127, np.int8)
+        xq_np[1] = -127
+        xq = torch.from_numpy(xq_np).to(DEV)
+        xs = torch.ones(m, dtype=torch.float32, device=DEV)
+        say("accumulator extremes", fn.__name__, m, n, k)
+        got = fn(xq, xs, layer, torch.int32).cpu().numpy().astype(np.int64)
+        ref = O.gemm_exact(xq_np, O.decode_w4(packed, srel, cb))
+        assert ref.min() == -127 * 128 * k and ref.max() == 127 * 128 * k
+        assert np.array_equal(got, ref)
