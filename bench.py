@@ -77,14 +77,16 @@ def bench_prefill(args, torch, B, device):
     from bit_codebook_quantized_amd import synth
     M, N, K = 2048, 4096, 4096
     w = torch.from_numpy(synth.gaussian_weight(N, K, seed=synth.seed_for(2, 0, synth.ROLE_WEIGHT))).to(device)
-    make_layer(B, w)                                   # warm-up of the quantiser
-    ev = event_pairs(torch, 1)[0]
+    cb = torch.tensor(B.FIXED_CODEBOOK, dtype=torch.float32, device=device)
+    B.quantize_w4(w, cb)                               # warm-up of the quantiser
+    pairs = event_pairs(torch, 5)
     torch.cuda.synchronize()
-    ev[0].record()
-    layer = make_layer(B, w)
-    ev[1].record()
+    for a, b in pairs:
+        a.record()
+        layer = B.quantize_w4(w, cb)
+        b.record()
     torch.cuda.synchronize()
-    quant_ms = ev[0].elapsed_time(ev[1])
+    quant_ms = mean_ms(pairs)
     host = host_copy(layer)
     del w
     x_np = synth.activations(M, K, seed=synth.seed_for(2, 0, synth.ROLE_ACT), kind="outliers",
