@@ -50,6 +50,7 @@ template <int R>
 struct Batch {
     uint4 q[2][R];
     uint32_t s[R];
+    float w[R], b[R];   // the rows' channel scales and biases (epilogue operands)
 };
 
 // Loads are unconditional (lanes past the row end re-read its last 4 groups), so the
@@ -233,12 +234,14 @@ __device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds,
 
 // FUSED: the activations arrive as bf16 rows x (rotated and quantised in the block, see
 // rotate_quant_to_lds; K <= slab_cols(MM)) instead of xq / xs.
-template <int MM, int R, bool FUSED = false, bool LONGK = false>
+// CARRY: the tile's channel scales and biases are loaded with each batch (for blocks that
+// walk several tiles); otherwise they are loaded once, in the tile's epilogue.
+template <int MM, int R, bool FUSED = false, bool LONGK = false, bool CARRY = false>
 __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const float* __restrict__ xs,
                                           const uint8_t* __restrict__ qp, const uint8_t* __restrict__ srel,
                                           const float* __restrict__ codebook, const float* __restrict__ ws,
                                           const float* __restrict__ bias, int N, int K, int out_type,
-                                          void* __restrict__ out, int tile0, int ntile,
+                                          void* __restrict__ out, int tile0, int ntile, int tstride,
                                           const uint16_t* __restrict__ x = nullptr, int qmax = 127,
                                           int8_t* __restrict__ xq_out = nullptr, float* __restrict__ xs_out = nullptr) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -253,7 +256,7 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
     const int KH = K >> 1, G = K >> 4, nchunk = K >> 4;
     // the work is a sequence of steps (tile t, batch gb): batch gb covers groups
     // 256*gb .. 256*gb + 255 of each of the tile's rows; tile t covers rows
-    // 4R*(tile0 + t) ..; wave w takes R consecutive rows of it
+    // 4R*(tile0 + t*tstride) ..; wave w takes R consecutive rows of it
     const int nbt = (nchunk + 64 * GV_BATCH - 1) / (64 * GV_BATCH);
     const int nsteps = ntile * nbt;
     auto issue = [&](Batch<R>& dst, int step) __attribute__((always_inline)) {
@@ -263,11 +266,23 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
         const uint8_t* sr[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int n = min(((tile0 + t) * WAVES + wave) * R + r, N - 1);
+            const int n = min(((tile0 + t * tstride) * WAVES + wave) * R + r, N - 1);
             qr[r] = qp + (int64_t)n * KH;
             sr[r] = srel + (int64_t)n * G;
         }
         load_batch<R>(dst, qr, sr, 4 * lane + gb * 64 * GV_BATCH, nchunk);
+        if constexpr (CARRY) {
+            // the epilogue operands travel with the batch: loaded at the tile's end, after
+            // the next prefetch, the wait for them would drain that prefetch at every tile
+            // boundary
+            const float* bsrc = bias ? bias : ws;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int n = min(((tile0 + t * tstride) * WAVES + wave) * R + r, N - 1);
+                dst.w[r] = ws[n];
+                dst.b[r] = bsrc[n];
+            }
+        }
     };
 
     float* xs_w = reinterpret_cast<float*>(act + MM * SLAB);   // the rows' activation scales
@@ -380,16 +395,25 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
 #pragma unroll
             for (int o = 32 >> L; o >= 1; o >>= 1) v[0] += __shfl_xor(v[0], o, 64);
 
-            const int n0 = ((tile0 + t) * WAVES + wave) * R;
+            const int n0 = ((tile0 + t * tstride) * WAVES + wave) * R;
             const int idx = lane >> (6 - L);
             const int r = idx / MM, m = idx - r * MM;
-            // per-row epilogue operands: wave-uniform addresses (scalar loads)
-            float wn = ws[min(n0, N - 1)], bn = bias ? bias[min(n0, N - 1)] : 0.0f;
+            float wv[R], bv[R];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                if constexpr (CARRY) {
+                    wv[i] = cur.w[i];
+                    bv[i] = cur.b[i];
+                } else {   // wave-uniform addresses
+                    wv[i] = ws[min(n0 + i, N - 1)];
+                    bv[i] = bias ? bias[min(n0 + i, N - 1)] : 0.0f;
+                }
+            }
+            float wn = wv[0], bn = bv[0];
 #pragma unroll
             for (int i = 1; i < R; ++i) {
-                const float wi = ws[min(n0 + i, N - 1)], bi = bias ? bias[min(n0 + i, N - 1)] : 0.0f;
-                wn = r == i ? wi : wn;
-                bn = r == i ? bi : bn;
+                wn = r == i ? wv[i] : wn;
+                bn = r == i ? bv[i] : bn;
             }
             const float xm = xs_lds[m < MM ? m : 0];
             const int n = n0 + r;
@@ -426,7 +450,9 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(const int8_t* __restri
                                                           const float* __restrict__ ws,
                                                           const float* __restrict__ bias, int N, int K,
                                                           int out_type, void* __restrict__ out) {
-    gemv_body<MM, R>(xq, xs, qp, srel, codebook, ws, bias, N, K, out_type, out, blockIdx.x, 1);
+    // carrying the epilogue operands measured faster for several rows, slower for one
+    gemv_body<MM, R, false, false, (MM > 1)>(xq, xs, qp, srel, codebook, ws, bias, N, K, out_type, out, blockIdx.x, 1,
+                                             1);
 }
 
 template <int MM, int R, bool LONGK>
@@ -439,7 +465,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_act_kernel(const uint16_t* __
                                                               int out_type, void* __restrict__ out,
                                                               int8_t* __restrict__ xq_out, float* __restrict__ xs_out) {
     const bool first = blockIdx.x == 0;   // one block writes the prepared activations out
-    gemv_body<MM, R, true, LONGK>(nullptr, nullptr, qp, srel, codebook, ws, bias, N, K, out_type, out, blockIdx.x, 1, x,
+    gemv_body<MM, R, true, LONGK>(nullptr, nullptr, qp, srel, codebook, ws, bias, N, K, out_type, out, blockIdx.x, 1, 1, x,
                            qmax, first ? xq_out : nullptr, first ? xs_out : nullptr);
 }
 
@@ -462,10 +488,12 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_grouped_kernel(const GroupArg
     const w4a8_gemv_layer& L = args.layer[l];
     const int per_tile = (GV_THREADS / 64) * R;
     const int tiles = (int)((L.N + per_tile - 1) / per_tile);
-    const int tile0 = ((int)blockIdx.x - args.first[l]) * args.tiles_per_block;
-    const int ntile = min(args.tiles_per_block, tiles - tile0);
-    gemv_body<MM, R>(L.xq, L.xs, L.qpacked, L.srel, L.codebook, L.s_channel, L.bias, (int)L.N, (int)L.K,
-                     out_type, L.out, tile0, ntile);
+    // the layer's nblk blocks take its tiles round robin (block bl: tiles bl, bl + nblk, ...), so
+    // the blocks running at one time read neighbouring rows
+    const int nblk = args.first[l + 1] - args.first[l], bl = (int)blockIdx.x - args.first[l];
+    const int ntile = (tiles - bl + nblk - 1) / nblk;
+    gemv_body<MM, R, false, false, true>(L.xq, L.xs, L.qpacked, L.srel, L.codebook, L.s_channel, L.bias, (int)L.N,
+                                         (int)L.K, out_type, L.out, bl, ntile, nblk);
 }
 
 // rows per wave: 2 when that still gives >= 2048 waves (8 per compute unit), else 1
