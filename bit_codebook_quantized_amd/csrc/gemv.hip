@@ -36,6 +36,7 @@ namespace {
 constexpr int GV_THREADS = 256;
 constexpr int GV_BATCH = 4;   // groups per lane per batch
 constexpr int GEMV_GROUP_MAX = 32;   // layers per grouped launch (the table fits the kernel arguments)
+constexpr int64_t GV_GROUP_BLOCKS = 4096;   // blocks a grouped call is cut into (all its launches)
 
 constexpr int pow2_ceil(int v) { return v <= 1 ? 1 : 2 * pow2_ceil((v + 1) / 2); }
 constexpr int log2i(int v) { return v <= 1 ? 0 : 1 + log2i(v / 2); }
@@ -72,6 +73,35 @@ __device__ __forceinline__ void load_batch(Batch<R>& b, const uint8_t* const (&q
 // bank groups.
 __device__ __forceinline__ int act_chunk(int c) { return c ^ ((c >> 4) & 3); }
 
+// Inside a chunk each 8-column half is stored even columns first: bytes k0 k2 k4 k6 k1 k3
+// k5 k7, the order in which decode_split returns the weights, so the products need no
+// re-interleave of the decoded bytes.
+__device__ __forceinline__ uint4 act_split(uint4 v) {
+    return uint4{perm(v.y, v.x, 0x06040200u), perm(v.y, v.x, 0x07050301u), perm(v.w, v.z, 0x06040200u),
+                 perm(v.w, v.z, 0x07050301u)};
+}
+__device__ __forceinline__ uint4 act_merge(uint4 v) {   // inverse of act_split
+    return uint4{perm(v.y, v.x, 0x05010400u), perm(v.y, v.x, 0x07030602u), perm(v.w, v.z, 0x05010400u),
+                 perm(v.w, v.z, 0x07030602u)};
+}
+// byte position of column j (0..15) of a chunk
+__device__ __forceinline__ int act_byte(int j) { return (j & 8) | ((j & 1) << 2) | ((j >> 1) & 3); }
+
+// The 8 codes of one packed dword (byte i = code 2i | code 2i+1 << 4) against the
+// 16-level row t = {L0..3, L4..7, L8..11, L12..15}: .x = the levels of columns 0, 2, 4, 6,
+// .y = those of columns 1, 3, 5, 7.  `id` is 0x03020100 held in a register (so the merge
+// selector is one and-or).
+__device__ __forceinline__ uint2 decode_split(uint32_t x, uint4 t, uint32_t id) {
+    const uint32_t se = x & 0x07070707u;           // even codes, low 3 bits
+    const uint32_t so = (x >> 4) & 0x07070707u;    // odd codes, low 3 bits
+    const uint32_t lo_e = perm(t.y, t.x, se), hi_e = perm(t.w, t.z, se);
+    const uint32_t lo_o = perm(t.y, t.x, so), hi_o = perm(t.w, t.z, so);
+    // bit 3 of each code picks the upper half of the table: selector i or i + 4
+    const uint32_t me = ((x >> 1) & 0x04040404u) | id;
+    const uint32_t mo = ((x >> 5) & 0x04040404u) | id;
+    return uint2{perm(hi_e, lo_e, me), perm(hi_o, lo_o, mo)};
+}
+
 // Activation staging: MM rows x cols bytes of xq from column k0 (cols <= slab_cols(MM))
 // -> act[m * slab_cols(MM) ...].  Every load is issued before the first wait; `between`
 // runs after the loads and before the stores (the GEMV issues its first weight batch
@@ -95,7 +125,7 @@ __device__ __forceinline__ void stage_acts_n(uint8_t* act, const int8_t* __restr
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int i = min((int)threadIdx.x + 256 * c, per_row - 1);
-            *reinterpret_cast<uint4*>(act + m * slab_cols(MM) + act_chunk(i) * 16) = v[m][c];
+            *reinterpret_cast<uint4*>(act + m * slab_cols(MM) + act_chunk(i) * 16) = act_split(v[m][c]);
         }
 }
 
@@ -196,7 +226,7 @@ __device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds,
         if ((nch == 1 || !pass1) && ok) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                act[row * SLAB + act_chunk(16 * blk + i) * 16 + l16] = (uint8_t)quant1(r[i], inv, qmaxf);
+                act[row * SLAB + act_chunk(16 * blk + i) * 16 + act_byte(l16)] = (uint8_t)quant1(r[i], inv, qmaxf);
         }
     };
 
@@ -227,7 +257,7 @@ __device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds,
         for (int i = tid; i < MM * per_row; i += GV_THREADS) {
             const int m = i / per_row, c = i - m * per_row;
             *reinterpret_cast<uint4*>(xq_out + (int64_t)m * K + c * 16) =
-                *reinterpret_cast<const uint4*>(act + m * SLAB + act_chunk(c) * 16);
+                act_merge(*reinterpret_cast<const uint4*>(act + m * SLAB + act_chunk(c) * 16));
         }
     }
 }
@@ -318,6 +348,8 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
 
     const float* xs_lds = xs_w;
     int32_t acc[R * MM];
+    uint32_t id = 0x03020100u;   // identity byte selector, kept in a register
+    asm volatile("" : "+v"(id));
     int slab_k0 = 0;
 
     // One step: prefetch the next step's batch into `nxt` (unconditionally, so the compiler
@@ -346,17 +378,20 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
         }
         const int jb = 4 * lane + gb * 64 * GV_BATCH;   // the lane's first group of the batch
         if (jb < nchunk) {                                // all 4 groups, or none (nchunk % 16 == 0)
+            // chunks c0 + u (c0 = a multiple of 4) sit at act_chunk(c0) ^ u: one address
+            // per batch, an xor per group
+            const int a0 = act_chunk(jb - (slab_k0 >> 4)) * 16;
 #pragma unroll
             for (int u = 0; u < GV_BATCH; ++u) {
-                const int ca = act_chunk(jb + u - (slab_k0 >> 4));
                 uint4 a[MM];
 #pragma unroll
-                for (int m = 0; m < MM; ++m) a[m] = *reinterpret_cast<const uint4*>(act + m * SLAB + ca * 16);
+                for (int m = 0; m < MM; ++m) a[m] = *reinterpret_cast<const uint4*>(act + m * SLAB + (a0 ^ (16 * u)));
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const uint4 tt = lut4[(cur.s[r] >> (8 * u)) & 0xFFu];
                     const uint4 qq = cur.q[u >> 1][r];
-                    const uint2 d0 = decode8((u & 1) ? qq.z : qq.x, tt), d1 = decode8((u & 1) ? qq.w : qq.y, tt);
+                    const uint2 d0 = decode_split((u & 1) ? qq.z : qq.x, tt, id),
+                                d1 = decode_split((u & 1) ? qq.w : qq.y, tt, id);
 #pragma unroll
                     for (int m = 0; m < MM; ++m) {
                         int32_t sacc = acc[r * MM + m];
@@ -471,18 +506,18 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_act_kernel(const uint16_t* __
 
 // Several independent layers (same M) in one launch: block b works on the layer whose
 // range [first[l], first[l+1]) of block ids holds b, as block b - first[l] of it, on
-// tiles_per_block consecutive row tiles (the level table and the activations are staged
+// every nblk-th row tile of the layer (the level table and the activations are staged
 // once per block; the first loads of a tile are issued during the last batch of the
 // previous one).  The layer table travels in the kernel arguments.
 struct GroupArgs {
     int count;
-    int tiles_per_block;
     int first[GEMV_GROUP_MAX + 1];
     w4a8_gemv_layer layer[GEMV_GROUP_MAX];
 };
 
+// for one activation row, at most 128 registers (4 waves per SIMD, measured faster than 3)
 template <int MM, int R>
-__global__ __launch_bounds__(GV_THREADS) void gemv_grouped_kernel(const GroupArgs args, int out_type) {
+__global__ __launch_bounds__(GV_THREADS, MM == 1 ? 4 : 1) void gemv_grouped_kernel(const GroupArgs args, int out_type) {
     int l = 0;
     while (l + 1 < args.count && (int)blockIdx.x >= args.first[l + 1]) ++l;   // uniform: a few steps
     const w4a8_gemv_layer& L = args.layer[l];
@@ -502,22 +537,25 @@ int rows_per_wave(int64_t rows) { return (rows + 1) / 2 >= 2048 ? 2 : 1; }
 
 template <int MM>
 hipError_t launch_gemv_grouped_m(const w4a8_gemv_layer* layers, int count, int out_type, hipStream_t stream) {
-    int64_t rows = 0;
+    int64_t rows = 0, steps = 0;
     for (int i = 0; i < count; ++i) rows += layers[i].N;
     const int R = out_type == 3 ? 2 : rows_per_wave(rows), per_tile = (GV_THREADS / 64) * R;   // SwiGLU pairs rows
-    // consecutive row tiles per block: enough blocks for a few rounds over the chip
-    // (256 compute units x 3 resident blocks x 4), fewer level-table builds per row
-    const int64_t total_tiles = (rows + per_tile - 1) / per_tile + count;
-    const int tpb = (int)(total_tiles / 3072 > 1 ? total_tiles / 3072 : 1);
+    // a tile of a layer with K columns takes nbt(K) steps of one weight batch each; blocks
+    // get about the same number of steps (not tiles), so that layers of different K end
+    // together, and the set is cut into about GV_GROUP_BLOCKS blocks (a few rounds over the
+    // chip: fewer, longer blocks leave a tail, more, shorter ones repeat the set-up)
+    auto tiles_of = [&](int i) { return (layers[i].N + per_tile - 1) / per_tile; };
+    auto nbt_of = [&](int i) { return (layers[i].K / 16 + 64 * GV_BATCH - 1) / (64 * GV_BATCH); };
+    for (int i = 0; i < count; ++i) steps += tiles_of(i) * nbt_of(i);
+    const int64_t per_block = steps / GV_GROUP_BLOCKS > 1 ? steps / GV_GROUP_BLOCKS : 1;
     for (int base = 0; base < count; base += GEMV_GROUP_MAX) {
         GroupArgs a;
         a.count = count - base < GEMV_GROUP_MAX ? count - base : GEMV_GROUP_MAX;
-        a.tiles_per_block = tpb;
         a.first[0] = 0;
         for (int i = 0; i < a.count; ++i) {
             a.layer[i] = layers[base + i];
-            const int tiles = (int)((layers[base + i].N + per_tile - 1) / per_tile);
-            a.first[i + 1] = a.first[i] + (tiles + tpb - 1) / tpb;
+            const int64_t tpb = per_block / nbt_of(base + i) > 1 ? per_block / nbt_of(base + i) : 1;
+            a.first[i + 1] = a.first[i] + (int)((tiles_of(base + i) + tpb - 1) / tpb);
         }
         for (int i = a.count; i < GEMV_GROUP_MAX; ++i) a.first[i + 1] = a.first[a.count];
         const size_t lds = gemv_lds_bytes(MM, false);
