@@ -99,18 +99,16 @@ def bench_prefill(args, torch, B, device):
     gemm_call = B.prepared_linear("w4a8_gemm", xq, xs, layer, out)
 
     def step(ev=None):
-        if ev is not None:
-            ev[0].record()
         rq_call()
-        if ev is not None:
-            ev[1].record()
+        if ev is not None:   # the GEMM's own duration (the roofline kernel), on its stream
+            ev[0].record()
         gemm_call()
         if ev is not None:
-            ev[2].record()
+            ev[1].record()
 
     for _ in range(args.warmup):
         step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = event_pairs(torch, args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -118,9 +116,11 @@ def bench_prefill(args, torch, B, device):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
     # step 0's events can include the host's first launch latency; the rest are queued
-    # behind the running GEMM, so they time the GPU alone
-    rq_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs[1:]]))
-    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs[1:]]))
+    # behind the running kernels, so they time the GPU alone
+    gemm_ms = mean_ms(evs[1:])
+    # rotate_quant_act alone, after the timed region (an event before it in every step would
+    # add a gap to the step)
+    rq_ms, _ = timed_launches(torch, [rq_call], 20, int(args.sleep_cycles))
     ops = 2.0 * M * N * K
     return dict(M=M, N=N, K=K, wall_s=wall, rq_ms=rq_ms, gemm_ms=gemm_ms, ops=ops, x_np=x_np, host=host,
                 quant_ms=quant_ms,

@@ -160,50 +160,103 @@ __global__ __launch_bounds__(RG_THREADS) void dequant_kernel(const uint8_t* __re
 }
 
 // The dequantised, rotated-back weight plus a low-rank delta (one block per row chunk).
-__global__ __launch_bounds__(RG_THREADS) void lora_merge_kernel(const uint8_t* __restrict__ qpacked,
+// LoRA merge: a block of LM_THREADS threads (LM_THREADS / 16 rotation blocks, LM_CHUNK
+// columns) merges LM_ROWS rows, so every A element it loads serves LM_ROWS rows (A is read
+// N / LM_ROWS times in all, from L2).  Thread t holds the deltas of columns
+// c0 + 16 t .. c0 + 16 t + 15 of each row in fp64; the B entries are block-uniform.
+constexpr int LM_THREADS = 128, LM_ROWS = 4, LM_CHUNK = LM_THREADS * 16;
+
+__global__ __launch_bounds__(LM_THREADS) void lora_merge_kernel(const uint8_t* __restrict__ qpacked,
                                                                 const uint8_t* __restrict__ srel,
                                                                 const float* __restrict__ codebook,
-                                                                const float* __restrict__ s_channel, int K,
-                                                                int nchunk, const float* __restrict__ lora_a,
+                                                                const float* __restrict__ s_channel, int64_t N,
+                                                                int K, int nchunk, const float* __restrict__ lora_a,
                                                                 const float* __restrict__ lora_b, int rank,
                                                                 float scale, float* __restrict__ out) {
-    __shared__ double tbuf[16 * 16 * QTSTRIDE];
-    __shared__ float fbuf[16 * (256 + 16)];
+    __shared__ double tbuf[(LM_THREADS / 16) * 16 * QTSTRIDE];
+    __shared__ float fbuf[(LM_THREADS / 16) * (256 + 16)];
     const int tid = threadIdx.x, slot = tid >> 4, l16 = tid & 15;
-    const int64_t row = blockIdx.x / nchunk;
-    const int c0 = (blockIdx.x - (int)(row * nchunk)) * RG_CHUNK;
+    const int64_t row0 = (int64_t)(blockIdx.x / nchunk) * LM_ROWS;
+    const int c0 = (int)(blockIdx.x % nchunk) * LM_CHUNK;
     const int col = c0 + tid * 16;
     const bool ok = col < K;
-    float w[16];
-    if (ok) {
-        const float s = e4m3fn_to_f32(srel[row * (K >> 4) + (col >> 4)]);
-        const float sch = s_channel[row];
-        const uint2 q = *reinterpret_cast<const uint2*>(qpacked + row * (K >> 1) + (col >> 1));
+
+    // delta[row][k] = sum over r, in order, of fp64(b[row][r]) * fp64(a[r][k]), each product
+    // and sum rounded in fp64
+    double d[LM_ROWS][16];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const uint32_t code = ((k < 8 ? q.x : q.y) >> (4 * (k & 7))) & 15u;
-            w[k] = __fmul_rn((float)(int8_t)(uint8_t)grid_level(codebook[code], s), sch);
+    for (int i = 0; i < LM_ROWS; ++i)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) d[i][k] = 0.0;
+    // B entries are block-uniform; an opaque per-lane zero offset makes their loads vector
+    // loads, counted in order with the A loads (scalar loads would each be waited for in turn)
+    int zero = 0;
+    asm volatile("" : "+v"(zero));
+    const float* brow[LM_ROWS];
+#pragma unroll
+    for (int i = 0; i < LM_ROWS; ++i) brow[i] = lora_b + (row0 + i < N ? row0 + i : N - 1) * rank + zero;
+    // A loads are unconditional (lanes past the row end read its last 16 columns, and their
+    // deltas are never stored) and alternate between two named buffers, so the loads of
+    // r + 1 are in flight while r is accumulated
+    const float* acol = lora_a + (ok ? col : K - 16);
+    struct Term {
+        float a[16], b[LM_ROWS];
+    };
+    auto load_term = [&](Term& t, int r) __attribute__((always_inline)) {
+        load16(acol + (int64_t)r * K, t.a);
+#pragma unroll
+        for (int i = 0; i < LM_ROWS; ++i) t.b[i] = brow[i][r];
+    };
+    auto accumulate = [&](const Term& t) __attribute__((always_inline)) {
+        double ad[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) ad[k] = (double)t.a[k];
+#pragma unroll
+        for (int i = 0; i < LM_ROWS; ++i) {
+            const double b = (double)t.b[i];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) d[i][k] = __dadd_rn(d[i][k], __dmul_rn(b, ad[k]));
         }
-    } else {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) w[k] = 0.0f;
+    };
+    Term tA, tB;
+    int r = 0;
+    if (rank > 0) {
+        load_term(tA, 0);
+        for (; r + 1 < rank; r += 2) {
+            load_term(tB, r + 1);
+            accumulate(tA);
+            load_term(tA, r + 2 < rank ? r + 2 : rank - 1);   // past the end: a reload
+            accumulate(tB);
+        }
+        if (r < rank) accumulate(tA);
     }
-    rotate16_in_place(w, slot, l16, tbuf, fbuf);   // block-uniform: back to the plain basis
-    if (!ok) return;
-    double d[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) d[k] = 0.0;
-    for (int r = 0; r < rank; ++r) {
-        const double b = (double)lora_b[row * rank + r];
-        float a[16];
-        load16(lora_a + (int64_t)r * K + col, a);
-#pragma unroll
-        for (int k = 0; k < 16; ++k) d[k] = __dadd_rn(d[k], __dmul_rn(b, (double)a[k]));
-    }
+
     const double sc = (double)scale;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) w[k] = __fadd_rn(w[k], (float)__dmul_rn(d[k], sc));
-    store16(out + row * K + col, w);
+    for (int i = 0; i < LM_ROWS; ++i) {
+        const int64_t row = row0 + i;
+        if (row >= N) break;   // block-uniform
+        float w[16];
+        if (ok) {
+            const float s = e4m3fn_to_f32(srel[row * (K >> 4) + (col >> 4)]);
+            const float sch = s_channel[row];
+            const uint2 q = *reinterpret_cast<const uint2*>(qpacked + row * (K >> 1) + (col >> 1));
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const uint32_t code = ((k < 8 ? q.x : q.y) >> (4 * (k & 7))) & 15u;
+                w[k] = __fmul_rn((float)(int8_t)(uint8_t)grid_level(codebook[code], s), sch);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) w[k] = 0.0f;
+        }
+        rotate16_in_place(w, slot, l16, tbuf, fbuf);   // all threads: back to the plain basis
+        if (ok) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) w[k] = __fadd_rn(w[k], (float)__dmul_rn(d[i][k], sc));
+            store16(out + row * K + col, w);
+        }
+    }
 }
 
 }  // namespace
@@ -212,9 +265,10 @@ hipError_t launch_lora_merge(const uint8_t* qpacked, const uint8_t* srel, const 
                              const float* s_channel, int64_t N, int K, const float* lora_a, const float* lora_b,
                              int rank, float scale, float* out, hipStream_t stream) {
     (void)hipGetLastError();
-    const int nchunk = (K + RG_CHUNK - 1) / RG_CHUNK;
-    hipLaunchKernelGGL(lora_merge_kernel, dim3((unsigned)(N * nchunk)), dim3(RG_THREADS), 0, stream, qpacked, srel,
-                       codebook, s_channel, K, nchunk, lora_a, lora_b, rank, scale, out);
+    const int nchunk = (K + LM_CHUNK - 1) / LM_CHUNK;
+    const int64_t blocks = (N + LM_ROWS - 1) / LM_ROWS * nchunk;
+    hipLaunchKernelGGL(lora_merge_kernel, dim3((unsigned)blocks), dim3(LM_THREADS), 0, stream, qpacked, srel,
+                       codebook, s_channel, N, K, nchunk, lora_a, lora_b, rank, scale, out);
     return hipGetLastError();
 }
 
