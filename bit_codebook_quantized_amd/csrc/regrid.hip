@@ -35,6 +35,15 @@ constexpr int RG_CHUNK = 4096;
 
 // Stochastic bracket choice ([AT] _assign_grid, stochastic branch) among 16
 // non-decreasing levels; comparisons with a NaN level are false.
+// The grid levels of a group are non-decreasing when the codebook is sorted ascending and
+// the group scale is not negative (NaN fails both tests).
+__device__ __forceinline__ bool levels_ascend(const float (&cb)[16], float s) {
+    bool a = s >= 0.0f;
+#pragma unroll
+    for (int c = 0; c < 15; ++c) a = a && cb[c] <= cb[c + 1];
+    return a;
+}
+
 __device__ __forceinline__ uint32_t stochastic16(float x, float u, const float (&lvl)[16]) {
     int p = 0;
 #pragma unroll
@@ -63,6 +72,9 @@ __device__ __forceinline__ void store16(float* __restrict__ p, const float (&v)[
     for (int i = 0; i < 4; ++i) reinterpret_cast<float4*>(p)[i] = float4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
 }
 
+// STOCH: stochastic rounding with the uniform draws u, else the nearest level (one path per
+// instantiation: with both in one kernel the compiler moved the level table to scratch).
+template <bool STOCH>
 __global__ __launch_bounds__(RG_THREADS) void requant_kernel(const float* __restrict__ wt, int K, int nchunk,
                                                              int rotated, const float* __restrict__ codebook,
                                                              const uint8_t* __restrict__ srel,
@@ -83,21 +95,28 @@ __global__ __launch_bounds__(RG_THREADS) void requant_kernel(const float* __rest
     for (int c = 0; c < 16; ++c) cb[c] = codebook[c];
     const float sch = s_channel[row];
     float lvl[16];
-    grid_levels16(cb, e4m3fn_to_f32(srel[row * (K >> 4) + (col >> 4)]), lvl);
+    const float s = e4m3fn_to_f32(srel[row * (K >> 4) + (col >> 4)]);
+    grid_levels16(cb, s, lvl);
     float r[16];
-    if (u) load16(u + row * K + col, r);
+    if constexpr (STOCH) load16(u + row * K + col, r);
+    const bool asc = !STOCH && levels_ascend(cb, s);
     uint32_t packed[2] = {0u, 0u};
+    if constexpr (STOCH) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const float t = __fdiv_rn(w[k], sch);
-        uint32_t code;
-        if (u) {
-            code = stochastic16(t, r[k], lvl);
-        } else {
+        for (int k = 0; k < 16; ++k)
+            packed[k >> 3] |= stochastic16(__fdiv_rn(w[k], sch), r[k], lvl) << (4 * (k & 7));
+    } else if (asc) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
             float dummy;
-            code = (uint32_t)nearest16_any(t, lvl, &dummy);
+            packed[k >> 3] |= (uint32_t)nearest16_sorted(__fdiv_rn(w[k], sch), lvl, &dummy) << (4 * (k & 7));
         }
-        packed[k >> 3] |= code << (4 * (k & 7));
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            float dummy;
+            packed[k >> 3] |= (uint32_t)nearest16_any(__fdiv_rn(w[k], sch), lvl, &dummy) << (4 * (k & 7));
+        }
     }
     *reinterpret_cast<uint2*>(qpacked + row * (K >> 1) + (col >> 1)) = uint2{packed[0], packed[1]};
 }
@@ -115,14 +134,17 @@ __global__ __launch_bounds__(RG_THREADS) void fake_quant_kernel(const float* __r
 #pragma unroll
     for (int c = 0; c < 16; ++c) cb[c] = codebook[c];
     float lvl[16];
-    grid_levels16(cb, e4m3fn_to_f32(srel[g]), lvl);
+    const float s = e4m3fn_to_f32(srel[g]);
+    grid_levels16(cb, s, lvl);
+    const bool asc = levels_ascend(cb, s);
     const float sch = s_channel[row];
     float w[16], y[16];
     load16(w_rot + g * 16, w);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         float lv;
-        (void)nearest16_any(__fdiv_rn(w[k], sch), lvl, &lv);
+        const float t = __fdiv_rn(w[k], sch);
+        (void)(asc ? nearest16_sorted(t, lvl, &lv) : nearest16_any(t, lvl, &lv));
         y[k] = __fmul_rn(lv, sch);
     }
     store16(out + g * 16, y);
@@ -277,8 +299,12 @@ hipError_t launch_requantize(const float* w, int64_t N, int K, int rotated, cons
                              hipStream_t stream) {
     (void)hipGetLastError();   // clear a stale error so the check below is about this launch
     const int nchunk = (K + RG_CHUNK - 1) / RG_CHUNK;
-    hipLaunchKernelGGL(requant_kernel, dim3((unsigned)(N * nchunk)), dim3(RG_THREADS), 0, stream, w, K, nchunk,
-                       rotated, codebook, srel, s_channel, u, qpacked);
+    if (u)
+        hipLaunchKernelGGL(requant_kernel<true>, dim3((unsigned)(N * nchunk)), dim3(RG_THREADS), 0, stream, w, K,
+                           nchunk, rotated, codebook, srel, s_channel, u, qpacked);
+    else
+        hipLaunchKernelGGL(requant_kernel<false>, dim3((unsigned)(N * nchunk)), dim3(RG_THREADS), 0, stream, w, K,
+                           nchunk, rotated, codebook, srel, s_channel, u, qpacked);
     return hipGetLastError();
 }
 

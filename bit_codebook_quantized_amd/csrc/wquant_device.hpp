@@ -46,11 +46,13 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn(float x) {
 // p clamped to 0..15, the upper one only if strictly closer (fp32 distances).
 // Returns the code; *lv receives the chosen level.
 //
-// nearest16 is for non-decreasing levels (a sorted codebook and a positive scale, as
-// in the quantiser): the candidates are then the last level below x and the first one
-// not below it, tracked in the same pass as the count.  nearest16_any takes the two
-// candidates by index, so it follows the rule for levels in any order (stored scale
-// bytes of either sign); for non-decreasing levels the two agree.
+// nearest16 and nearest16_sorted are for non-decreasing levels (a sorted codebook and a
+// non-negative scale, as in the quantiser): the candidates are then the last level below
+// x and the first one not below it.  nearest16 tracks them in the same pass as the count
+// (few registers: the quantiser's fit calls it three times per weight); nearest16_sorted
+// finds them by binary search (fewer instructions).  nearest16_any takes the two
+// candidates by index, so it follows the rule for levels in any order (stored scale bytes
+// of either sign); for non-decreasing levels all three agree.
 __device__ __forceinline__ int nearest16(float x, const float (&lvl)[16], float* lv) {
     int p = 0;
     float lo = lvl[0], hi = lvl[15];
@@ -68,16 +70,72 @@ __device__ __forceinline__ int nearest16(float x, const float (&lvl)[16], float*
     return up ? ihi : ilo;
 }
 
+// Copies the 16 levels into values produced by empty asm statements.  Selects between
+// table entries then act on those values; a select between two loads of the table is
+// otherwise turned into one load from a selected address, which keeps the caller's level
+// table in scratch memory.
+__device__ __forceinline__ void levels_in_registers(const float (&lvl)[16], float (&out)[16]) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        out[c] = lvl[c];
+        asm volatile("" : "+v"(out[c]));
+    }
+}
+
+// A branchless binary search: five tests give p = #{c : lvl[c] < x} (pivots 7; 3 or 11;
+// ...; then p itself), and, as in a search tree, the level below x is the last pivot that
+// tested below it and the level not below x the last one that did not (lvl[0] / lvl[15]
+// when there is none).
+__device__ __forceinline__ int nearest16_sorted(float x, const float (&lv16)[16], float* lv) {
+    float lvl[16];
+    levels_in_registers(lv16, lvl);
+    float lo = lvl[0], hi = lvl[15];
+    const bool t8 = lvl[7] < x;
+    lo = t8 ? lvl[7] : lo;
+    hi = t8 ? hi : lvl[7];
+    const float p4 = t8 ? lvl[11] : lvl[3];
+    const bool t4 = p4 < x;
+    lo = t4 ? p4 : lo;
+    hi = t4 ? hi : p4;
+    const float p2 = t8 ? (t4 ? lvl[13] : lvl[9]) : (t4 ? lvl[5] : lvl[1]);
+    const bool t2 = p2 < x;
+    lo = t2 ? p2 : lo;
+    hi = t2 ? hi : p2;
+    const float q0 = t2 ? lvl[2] : lvl[0], q1 = t2 ? lvl[6] : lvl[4], q2 = t2 ? lvl[10] : lvl[8],
+                q3 = t2 ? lvl[14] : lvl[12];
+    const float p1 = t8 ? (t4 ? q3 : q2) : (t4 ? q1 : q0);
+    const bool t1 = p1 < x;
+    lo = t1 ? p1 : lo;
+    hi = t1 ? hi : p1;
+    const int b = (t8 ? 8 : 0) + (t4 ? 4 : 0) + (t2 ? 2 : 0) + (t1 ? 1 : 0);   // p is b or b + 1
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = t1 ? lvl[2 * j + 1] : lvl[2 * j];
+    const float f0 = t2 ? e[1] : e[0], f1 = t2 ? e[3] : e[2], f2 = t2 ? e[5] : e[4], f3 = t2 ? e[7] : e[6];
+    const float pf = t8 ? (t4 ? f3 : f2) : (t4 ? f1 : f0);   // lvl[b]
+    const bool t0 = pf < x;
+    lo = t0 ? pf : lo;
+    hi = t0 ? hi : pf;
+    const int p = b + (t0 ? 1 : 0);
+    const int ilo = p > 0 ? p - 1 : 0, ihi = p < 15 ? p : 15;
+    const float dlo = __builtin_fabsf(__fsub_rn(x, lo)), dhi = __builtin_fabsf(__fsub_rn(x, hi));
+    const bool up = dhi < dlo;
+    *lv = up ? hi : lo;
+    return up ? ihi : ilo;
+}
+
 __device__ __forceinline__ int nearest16_any(float x, const float (&lvl)[16], float* lv) {
     int p = 0;
 #pragma unroll
     for (int c = 0; c < 16; ++c) p += lvl[c] < x ? 1 : 0;
     const int ilo = p > 0 ? p - 1 : 0, ihi = p < 15 ? p : 15;
-    float lo = lvl[0], hi = lvl[0];
+    float L[16];
+    levels_in_registers(lvl, L);
+    float lo = L[0], hi = L[0];
 #pragma unroll
     for (int c = 1; c < 16; ++c) {
-        lo = c == ilo ? lvl[c] : lo;
-        hi = c == ihi ? lvl[c] : hi;
+        lo = c == ilo ? L[c] : lo;
+        hi = c == ihi ? L[c] : hi;
     }
     const float dlo = __builtin_fabsf(__fsub_rn(x, lo)), dhi = __builtin_fabsf(__fsub_rn(x, hi));
     const bool up = dhi < dlo;
