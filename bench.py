@@ -8,13 +8,15 @@ GEMV sweep (M = 1, 2, 4, 8 on one N=K=4096 layer; each launch reads one of 64
 distinct weight copies, 605 MB > the 256 MB Infinity Cache, so weights come from
 HBM) and reports weight GB/s against the 8 TB/s HBM peak.
 
-Kernel durations come from HIP events recorded on the launch stream around every
-kernel inside the timed region.  Weights are seeded N(0, 0.02^2) fp32 draws,
-rotated and quantised on the GPU by quantize_w4 (timed once and reported on its
-own: it is an offline step, not part of the layer); activations are seeded
-synthetic draws.
+The GEMM's duration comes from HIP events recorded on the launch stream inside the
+timed region, on sampled steps: the mean interval of whole steps minus that of
+rotate_quant_act alone, both starting from an event before rotate_quant_act (an
+event delays the next launch by a few microseconds; the difference cancels it).
+Weights are seeded N(0, 0.02^2) fp32 draws, rotated and quantised on the GPU by
+quantize_w4 (timed over five calls and reported on its own: it is an offline step,
+not part of the layer); activations are seeded synthetic draws.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -42,7 +44,7 @@ def weight_bytes(n, k):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--gemv-launches", type=int, default=640)
     p.add_argument("--sleep-cycles", type=float, default=4e7,
@@ -52,7 +54,10 @@ def parse():
     p.add_argument("--no-training", action="store_true", help="skip the training-path and variant kernels")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device-to-device copy 5 times (counter calibration)")
-    return p.parse_args()
+    args = p.parse_args()
+    if args.steps < 4:
+        p.error("--steps must be at least 4 (the GEMM's events sample steps 1 and 3 of every 4)")
+    return args
 
 
 def make_layer(B, w):
@@ -98,26 +103,40 @@ def bench_prefill(args, torch, B, device):
     rq_call = B.prepared_rotate_quant(x, xq, xs)
     gemm_call = B.prepared_linear("w4a8_gemm", xq, xs, layer, out)
 
-    def step(ev=None):
-        rq_call()
-        if ev is not None:   # the GEMM's own duration (the roofline kernel), on its stream
-            ev[0].record()
-        gemm_call()
+    def step(ev=None, whole=True):
+        # ev: an event pair from before rotate_quant_act to after the GEMM (whole) or to
+        # after rotate_quant_act (not whole), on the launch stream
         if ev is not None:
+            ev[0].record()
+        rq_call()
+        if ev is not None and not whole:
+            ev[1].record()
+        gemm_call()
+        if ev is not None and whole:
             ev[1].record()
 
     for _ in range(args.warmup):
         step()
-    evs = event_pairs(torch, args.steps)
+    # The GEMM's duration from events in the timed region: steps 1, 5, 9, ... bracket the
+    # whole step and steps 3, 7, 11, ... only rotate_quant_act, both from an event before
+    # it, so the difference of the two means is the GEMM's time on the stream; each event
+    # costs the GPU a few microseconds (a marker the next launch waits behind), which the
+    # difference cancels and which sampling keeps out of most steps.  Step 0 is skipped:
+    # its events include the host's first launch latency.
+    whole = {i: event_pairs(torch, 1)[0] for i in range(1, args.steps, 4)}
+    part = {i: event_pairs(torch, 1)[0] for i in range(3, args.steps, 4)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        if i in whole:
+            step(whole[i], True)
+        elif i in part:
+            step(part[i], False)
+        else:
+            step()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
-    # step 0's events can include the host's first launch latency; the rest are queued
-    # behind the running kernels, so they time the GPU alone
-    gemm_ms = mean_ms(evs[1:])
+    gemm_ms = mean_ms(list(whole.values())) - mean_ms(list(part.values()))
     # rotate_quant_act alone, after the timed region (an event before it in every step would
     # add a gap to the step)
     rq_ms, _ = timed_launches(torch, [rq_call], 20, int(args.sleep_cycles))
