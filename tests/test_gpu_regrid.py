@@ -130,3 +130,40 @@ def test_full_size_layer_sampled_rows():
     assert np.array_equal(deq[rows].view(np.uint32), ref.view(np.uint32))
     ref = O.fake_quant_rotated(w_rot_np[rows], srel[rows], sch[rows], cb)
     assert np.array_equal(fq[rows].view(np.uint32), ref.view(np.uint32))
+
+
+def test_nearest_level_ties_exact_levels_and_duplicates():
+    # Targets placed exactly on grid levels, exactly half-way between neighbouring levels
+    # (the rule keeps the lower candidate on a tie), a quarter off a level, beyond both
+    # ends, and NaN; scale bytes of every kind: positive (non-decreasing levels), negative
+    # (non-increasing), zero and saturating (runs of equal levels), NaN.  The channel
+    # scale is a power of two, so w_rot / s_channel reproduces each target exactly.
+    n, k = 16, 1024
+    g = synth.rng(synth.seed_for(13, 3, 3))
+    cb = O.FIXED_CODEBOOK
+    srel = g.integers(0, 256, (n, k // 16)).astype(np.uint8)
+    srel[0, :6] = [0x7F, 0xFF, 0x00, 0x80, 0x7E, 0xFE]      # NaN, NaN, +0, -0, largest +-
+    srel[1, :] = g.integers(0x40, 0x58, k // 16)              # moderate positive scales
+    levels = O.grid_levels(cb, srel)                          # [n, G, 16]
+    sch = np.full(n, 2.0 ** -6, np.float32)
+    t = np.empty((n, k // 16, 16), np.float32)
+    for r in range(n):
+        for gi in range(k // 16):
+            lv = levels[r, gi]
+            picks = list(lv[g.integers(0, 16, 6)])                      # on a level
+            a, b = np.sort(lv[g.integers(0, 16, 2)])
+            picks += [(a + b) / 2, (a + b) / 2 + 0.25, a - 0.25, b + 0.25]   # ties and near-ties
+            picks += [lv.min() - 3, lv.max() + 3, 127.5, -127.5, 0.0, np.nan]
+            t[r, gi] = np.asarray(picks, np.float32)
+    w_rot = (t.reshape(n, k) * sch[:, None]).astype(np.float32)
+    assert np.array_equal((w_rot.reshape(n, k // 16, 16) / sch[:, None, None]).astype(np.float32), t,
+                          equal_nan=True)
+    layer = layer_of(np.zeros((n, k // 2), np.uint8), srel, sch, cb)
+    say("nearest level: ties, exact levels, duplicate levels")
+    got = B.requantize_codes(dev(w_rot), layer, rotated=True).cpu().numpy()
+    assert np.array_equal(got, O.requantize_codes(w_rot, srel, sch, cb, rotated=True))
+    got = B.fake_quant(dev(w_rot), layer).cpu().numpy()
+    ref = O.fake_quant_rotated(w_rot, srel, sch, cb)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
