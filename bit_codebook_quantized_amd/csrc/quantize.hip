@@ -43,7 +43,7 @@ __global__ __launch_bounds__(QZ_THREADS) void quantize_kernel(const float* __res
                                                               uint8_t* __restrict__ srel,
                                                               float* __restrict__ s_channel) {
     __shared__ double tbuf[16 * 16 * QTSTRIDE];
-    __shared__ float fbuf[16 * (256 + 16)];
+    float* const fbuf = reinterpret_cast<float*>(tbuf);   // reused after the fp64 transpose
     __shared__ float wmax[QZ_THREADS / 64];
 
     const int tid = threadIdx.x, slot = tid >> 4, l16 = tid & 15, lane = tid & 63;

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(RG_THREADS) void requant_kernel(const float* __rest
                                                              const float* __restrict__ u,
                                                              uint8_t* __restrict__ qpacked) {
     __shared__ double tbuf[16 * 16 * QTSTRIDE];
-    __shared__ float fbuf[16 * (256 + 16)];
+    float* const fbuf = reinterpret_cast<float*>(tbuf);   // reused after the fp64 transpose
     const int tid = threadIdx.x, slot = tid >> 4, l16 = tid & 15;
     const int64_t row = blockIdx.x / nchunk;
     const int c0 = (blockIdx.x - (int)(row * nchunk)) * RG_CHUNK;
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(RG_THREADS) void dequant_kernel(const uint8_t* __re
                                                              const float* __restrict__ s_channel, int K, int nchunk,
                                                              int rotate_back, float* __restrict__ out) {
     __shared__ double tbuf[16 * 16 * QTSTRIDE];
-    __shared__ float fbuf[16 * (256 + 16)];
+    float* const fbuf = reinterpret_cast<float*>(tbuf);   // reused after the fp64 transpose
     const int tid = threadIdx.x, slot = tid >> 4, l16 = tid & 15;
     const int64_t row = blockIdx.x / nchunk;
     const int c0 = (blockIdx.x - (int)(row * nchunk)) * RG_CHUNK;
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(LM_THREADS) void lora_merge_kernel(const uint8_t* _
                                                                 const float* __restrict__ lora_b, int rank,
                                                                 float scale, float* __restrict__ out) {
     __shared__ double tbuf[(LM_THREADS / 16) * 16 * QTSTRIDE];
-    __shared__ float fbuf[(LM_THREADS / 16) * (256 + 16)];
+    float* const fbuf = reinterpret_cast<float*>(tbuf);   // reused after the fp64 transpose
     const int tid = threadIdx.x, slot = tid >> 4, l16 = tid & 15;
     const int64_t row0 = (int64_t)(blockIdx.x / nchunk) * LM_ROWS;
     const int c0 = (int)(blockIdx.x % nchunk) * LM_CHUNK;

@@ -170,7 +170,10 @@ __device__ __forceinline__ float fit_group(const float (&w)[16], const float (&c
 
 // Rotate the 16 fp32 values a thread holds -- columns 16*l16 .. 16*l16 + 15 of rotation
 // block `slot` -- in place: afterwards w[k] is the rotated value of the same column,
-// rounded once to fp32.  All threads of the block call it (it synchronises).
+// rounded once to fp32.  All threads of the block call it (it synchronises).  fbuf
+// (16 x 272 floats per slot) may alias tbuf (16 x 16 x QTSTRIDE doubles per slot): it is
+// written only after the barrier that ends the reads of tbuf.
+static_assert(16 * (256 + 16) * sizeof(float) <= 16 * 16 * QTSTRIDE * sizeof(double), "fbuf fits in tbuf");
 __device__ __forceinline__ void rotate16_in_place(float (&w)[16], int slot, int l16, double* tbuf, float* fbuf) {
     double v[16];
 #pragma unroll
