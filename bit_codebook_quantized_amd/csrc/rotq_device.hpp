@@ -21,8 +21,12 @@
 
 namespace w4a8 {
 
-constexpr int TSTRIDE = 17;   // padded row of the fp64 transpose buffer (bank spread)
-constexpr int ROTQ_TBUF_DOUBLES = 16 * 16 * TSTRIDE;   // one 16 x 16 tile per slot
+// The 16 x 16 fp64 transpose of a slot goes through LDS in two halves of 8 columns, each
+// a 16 x 8 tile with rows padded to 9 doubles: the 16 lanes' writes (72-byte stride) and
+// reads (consecutive doubles) each cover the 32 banks once.  Half the buffer of a whole
+// tile, so twice the blocks fit per compute unit.
+constexpr int TSTRIDE = 9;
+constexpr int ROTQ_TBUF_DOUBLES = 16 * 16 * TSTRIDE;   // one 16 x 8 tile per slot, 16 slots
 
 __device__ __forceinline__ void radix4(double& a0, double& a1, double& a2, double& a3) {
     const double s = (a0 + a1) + (a2 + a3);
@@ -65,12 +69,20 @@ __device__ __forceinline__ void rotate_loaded(const RotIn in, bool ok, int slot,
     }
     radix16(v);     // digits 0, 1 of the input column (inside the lane)
     double* t = tbuf + slot * (16 * TSTRIDE);
+    double u[16];   // column l16 of the slot's tile: u[j] = lane j's v[l16]
 #pragma unroll
-    for (int i = 0; i < 16; ++i) t[l16 * TSTRIDE + i] = v[i];
-    __syncthreads();
+    for (int h = 0; h < 2; ++h) {   // columns 8h .. 8h + 7, read by lanes 8h .. 8h + 7
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = t[j * TSTRIDE + l16];
-    __syncthreads();
+        for (int i = 0; i < 8; ++i) t[l16 * TSTRIDE + i] = v[8 * h + i];
+        __syncthreads();
+        if ((l16 >> 3) == h) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) u[j] = t[j * TSTRIDE + (l16 & 7)];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = u[j];
     radix16(v);     // digits 2, 3 (the lane index of the first half)
 #pragma unroll
     for (int i = 0; i < 16; ++i) r[i] = (float)(v[i] * 0.0625);
