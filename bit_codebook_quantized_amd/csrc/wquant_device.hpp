@@ -11,7 +11,7 @@
 
 namespace w4a8 {
 
-constexpr int QTSTRIDE = 17;     // padded row of the fp64 transpose buffer
+constexpr int QTSTRIDE = 9;      // padded row of the fp64 transpose buffer (16 x 8 halves)
 
 __device__ __forceinline__ void qradix4(double& a0, double& a1, double& a2, double& a3) {
     const double s = (a0 + a1) + (a2 + a3);
@@ -171,21 +171,31 @@ __device__ __forceinline__ float fit_group(const float (&w)[16], const float (&c
 // Rotate the 16 fp32 values a thread holds -- columns 16*l16 .. 16*l16 + 15 of rotation
 // block `slot` -- in place: afterwards w[k] is the rotated value of the same column,
 // rounded once to fp32.  All threads of the block call it (it synchronises).  fbuf
-// (16 x 272 floats per slot) may alias tbuf (16 x 16 x QTSTRIDE doubles per slot): it is
-// written only after the barrier that ends the reads of tbuf.
+// (272 floats per slot) may alias tbuf (16 x QTSTRIDE doubles per slot): it is written
+// only after the barrier that ends the reads of tbuf.
 static_assert(16 * (256 + 16) * sizeof(float) <= 16 * 16 * QTSTRIDE * sizeof(double), "fbuf fits in tbuf");
 __device__ __forceinline__ void rotate16_in_place(float (&w)[16], int slot, int l16, double* tbuf, float* fbuf) {
     double v[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) v[k] = (double)w[k];
     qradix16(v);   // digits 0, 1 of the column within the block (inside the thread)
+    // transpose of the slot's 16 x 16 tile in two 16 x 8 halves, rows padded to 9 doubles
+    // (conflict-free writes and reads; half the buffer of a whole tile)
     double* t = tbuf + slot * (16 * QTSTRIDE);
+    double u[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) t[l16 * QTSTRIDE + i] = v[i];
-    __syncthreads();
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = t[j * QTSTRIDE + l16];
-    __syncthreads();
+        for (int i = 0; i < 8; ++i) t[l16 * QTSTRIDE + i] = v[8 * h + i];
+        __syncthreads();
+        if ((l16 >> 3) == h) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) u[j] = t[j * QTSTRIDE + (l16 & 7)];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = u[j];
     qradix16(v);   // digits 2, 3; v[i] is now column 16*i + l16 of the block
     float* f = fbuf + slot * (256 + 16);
 #pragma unroll
