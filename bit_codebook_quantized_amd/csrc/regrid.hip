@@ -44,6 +44,26 @@ __device__ __forceinline__ bool levels_ascend(const float (&cb)[16], float s) {
     return a;
 }
 
+// The 16 grid levels of one scale as a packed byte row (level c in byte c % 4 of word
+// c / 4), the operand of decode8.
+__device__ __forceinline__ uint4 level_row(const float (&cb)[16], float s) {
+    uint32_t tw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        tw[j] = grid_level(cb[4 * j], s) | grid_level(cb[4 * j + 1], s) << 8 | grid_level(cb[4 * j + 2], s) << 16 |
+                grid_level(cb[4 * j + 3], s) << 24;
+    return uint4{tw[0], tw[1], tw[2], tw[3]};
+}
+
+// One group's 16 weights (codes q, 8 bytes) as fp32(level * s_channel): a byte-permute
+// decode against the level row, no per-weight codebook reads.
+__device__ __forceinline__ void decode_group_f32(uint2 q, uint4 t, float sch, float (&w)[16]) {
+    const uint2 d0 = decode8(q.x, t), d1 = decode8(q.y, t);
+    const uint32_t d[4] = {d0.x, d0.y, d1.x, d1.y};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) w[k] = __fmul_rn((float)(int8_t)(uint8_t)(d[k >> 2] >> (8 * (k & 3))), sch);
+}
+
 __device__ __forceinline__ uint32_t stochastic16(float x, float u, const float (&lvl)[16]) {
     int p = 0;
 #pragma unroll
@@ -162,17 +182,15 @@ __global__ __launch_bounds__(RG_THREADS) void dequant_kernel(const uint8_t* __re
     const int c0 = (blockIdx.x - (int)(row * nchunk)) * RG_CHUNK;
     const int col = c0 + tid * 16;
     const bool ok = col < K;
+    float cb[16];   // uniform loads
+#pragma unroll
+    for (int c = 0; c < 16; ++c) cb[c] = codebook[c];
     float w[16];
     if (ok) {
         const float s = e4m3fn_to_f32(srel[row * (K >> 4) + (col >> 4)]);
         const float sch = s_channel[row];
         const uint2 q = *reinterpret_cast<const uint2*>(qpacked + row * (K >> 1) + (col >> 1));
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const uint32_t code = ((k < 8 ? q.x : q.y) >> (4 * (k & 7))) & 15u;
-            const float w8 = (float)(int8_t)(uint8_t)grid_level(codebook[code], s);
-            w[k] = __fmul_rn(w8, sch);
-        }
+        decode_group_f32(q, level_row(cb, s), sch, w);
     } else {
 #pragma unroll
         for (int k = 0; k < 16; ++k) w[k] = 0.0f;
@@ -254,6 +272,9 @@ __global__ __launch_bounds__(LM_THREADS) void lora_merge_kernel(const uint8_t* _
     }
 
     const double sc = (double)scale;
+    float cb[16];   // uniform loads
+#pragma unroll
+    for (int c = 0; c < 16; ++c) cb[c] = codebook[c];
 #pragma unroll
     for (int i = 0; i < LM_ROWS; ++i) {
         const int64_t row = row0 + i;
@@ -263,11 +284,7 @@ __global__ __launch_bounds__(LM_THREADS) void lora_merge_kernel(const uint8_t* _
             const float s = e4m3fn_to_f32(srel[row * (K >> 4) + (col >> 4)]);
             const float sch = s_channel[row];
             const uint2 q = *reinterpret_cast<const uint2*>(qpacked + row * (K >> 1) + (col >> 1));
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const uint32_t code = ((k < 8 ? q.x : q.y) >> (4 * (k & 7))) & 15u;
-                w[k] = __fmul_rn((float)(int8_t)(uint8_t)grid_level(codebook[code], s), sch);
-            }
+            decode_group_f32(q, level_row(cb, s), sch, w);
         } else {
 #pragma unroll
             for (int k = 0; k < 16; ++k) w[k] = 0.0f;
