@@ -9,18 +9,19 @@
 // weight), which bounds the kernel by HBM bandwidth.
 //
 // Layout.  A block of 256 threads = 4 waves; wave w owns R consecutive output rows.
-// Its 64 lanes split K into 16-column groups (8 bytes of codes + 1 scale byte):
-// lane l takes groups l, l+64, l+128, ... so each load instruction reads 512
-// contiguous bytes of a row.  Groups are processed in batches of 4 per lane (4096
-// columns per wave); a batch's weight loads for all R rows are issued together and
-// the next batch is prefetched while the current one is decoded, so the bytes in
-// flight per compute unit cover HBM latency.  The first batch is issued before the
-// block builds its 256 x 16 level table in LDS and stages the int8 activations
-// (M x up to 32 KiB, reused by all R rows of all 4 waves) in LDS.
+// Its 64 lanes split K into 16-column groups (8 bytes of codes + 1 scale byte).  A
+// batch covers 4096 columns: lane l takes the 4 consecutive groups 4l .. 4l + 3 of
+// each row (two 16-byte code loads and one scale dword per row, each instruction
+// reading contiguous memory).  A batch's weight loads for all R rows are issued
+// together and the next batch is prefetched while the current one is decoded.  The
+// first batch is issued before the block builds its 256 x 16 level table in LDS and
+// stages the int8 activations (M x up to 32 KiB, reused by all R rows of all 4
+// waves) in LDS.
 //
 // Arithmetic per 16-column group and row: one LDS read of the 16-level table row
-// of the group's scale byte, two 8-code byte-permute decodes, and 4 v_dot4_i32_i8
-// per activation row.  The int32 partial sums of the R x M outputs stay in
+// of the group's scale byte, two 8-code byte-permute decodes that return even
+// columns before odd ones (the activation slab is stored in that order), and 4
+// v_dot4_i32_i8 per activation row.  The int32 partial sums of the R x M outputs stay in
 // registers for the whole of K and are combined across the wave once, by a
 // reduce-scatter (each halving step exchanges half the values), so a lane ends
 // with one fully summed output.
