@@ -246,6 +246,83 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     // ---- epilogue: accumulator (mt, nb) register r of lane l holds column
     // 16*nb + 4*(l/16) + r of row 32*wave + 16*mt + l%16
     const bool vec = m0 + BM <= M && n0 + BN <= N && (N & 3) == 0;
+    // bf16 and SwiGLU outputs of a whole tile (rows 16-byte aligned): each wave passes its
+    // 16-row halves through LDS (the weight buffers, free after the last barrier; rows
+    // padded by 16 bytes, so the narrow writes of 16 rows and the 16-byte reads along a row
+    // are conflict-free) and stores whole rows (4 x 256 or 8 x 128 bytes per instruction)
+    // instead of 32- or 16-byte pieces of 16 rows.  Measured ~2 us faster on the 53 us
+    // prefill product.
+    if (OUT == 3 && vec && (N & 15) == 0) {
+        constexpr int OPITCH = 144;   // 64 bf16 outputs per row + 16
+        uint8_t* ob = reinterpret_cast<uint8_t*>(&Bs[0][0]) + wave * (16 * OPITCH);
+        const int rl = lane & 15, cq = lane >> 4;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const float xsm = xs_t[32 * wave + 16 * mt + rl];
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                const int nl = 16 * nb + 4 * cq;
+                const float4 wv = *reinterpret_cast<const float4*>(&ws_t[nl]);
+                const float4 bv = *reinterpret_cast<const float4*>(&bias_t[nl]);
+                const v4i a = acc[mt][nb];
+                const float wsv[4] = {wv.x, wv.y, wv.z, wv.w}, bsv[4] = {bv.x, bv.y, bv.z, bv.w};
+                float y[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    y[r] = __fmul_rn((float)a[r], __fmul_rn(xsm, wsv[r]));
+                    if (bias) y[r] = __fadd_rn(y[r], bsv[r]);
+                }
+                // gate/up pairs (nl, nl + 1), (nl + 2, nl + 3) -> output columns nl/2, nl/2 + 1
+                *reinterpret_cast<uint32_t*>(ob + rl * OPITCH + nl) =
+                    f32x2_to_bf16x2(swiglu_f32(y[0], y[1]), swiglu_f32(y[2], y[3]));
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = (lane >> 3) + 8 * i, c = lane & 7;
+                const uint4 v = *reinterpret_cast<const uint4*>(ob + row * OPITCH + 16 * c);
+                const int64_t m = m0 + 32 * wave + 16 * mt + row;
+                *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + m * (N >> 1) + (n0 >> 1) + 8 * c) = v;
+            }
+            __syncthreads();
+        }
+        return;
+    }
+    if (OUT == 0 && vec && (N & 7) == 0) {
+        constexpr int OPITCH = 272;   // 128 bf16 outputs per row + 16
+        uint8_t* ob = reinterpret_cast<uint8_t*>(&Bs[0][0]) + wave * (16 * OPITCH);
+        const int rl = lane & 15, cq = lane >> 4;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const float xsm = xs_t[32 * wave + 16 * mt + rl];
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                const int nl = 16 * nb + 4 * cq;
+                const float4 wv = *reinterpret_cast<const float4*>(&ws_t[nl]);
+                const float4 bv = *reinterpret_cast<const float4*>(&bias_t[nl]);
+                const v4i a = acc[mt][nb];
+                const float wsv[4] = {wv.x, wv.y, wv.z, wv.w}, bsv[4] = {bv.x, bv.y, bv.z, bv.w};
+                float y[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    y[r] = __fmul_rn((float)a[r], __fmul_rn(xsm, wsv[r]));
+                    if (bias) y[r] = __fadd_rn(y[r], bsv[r]);
+                }
+                *reinterpret_cast<uint2*>(ob + rl * OPITCH + 2 * nl) =
+                    uint2{f32x2_to_bf16x2(y[0], y[1]), f32x2_to_bf16x2(y[2], y[3])};
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = cq + 4 * i;
+                const uint4 v = *reinterpret_cast<const uint4*>(ob + row * OPITCH + 16 * rl);
+                const int64_t m = m0 + 32 * wave + 16 * mt + row;
+                *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + m * N + n0 + 8 * rl) = v;
+            }
+            __syncthreads();
+        }
+        return;
+    }
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
         const int ml = 32 * wave + 16 * mt + (lane & 15), m = m0 + ml;
@@ -267,18 +344,18 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
             if (OUT == 3) {
                 // gate/up pairs (n, n + 1) and (n + 2, n + 3) -> columns n/2, n/2 + 1 of [M, N/2]
                 uint16_t* o = reinterpret_cast<uint16_t*>(out) + (int64_t)m * (N >> 1) + (n >> 1);
-                const uint16_t s0 = f32_to_bf16(swiglu_f32(y[0], y[1])), s1 = f32_to_bf16(swiglu_f32(y[2], y[3]));
+                const uint32_t s01 = f32x2_to_bf16x2(swiglu_f32(y[0], y[1]), swiglu_f32(y[2], y[3]));
                 if (vec) {
-                    *reinterpret_cast<uint32_t*>(o) = (uint32_t)s0 | ((uint32_t)s1 << 16);
+                    *reinterpret_cast<uint32_t*>(o) = s01;
                 } else if (m < M) {
-                    if (n + 1 < N) o[0] = s0;
-                    if (n + 3 < N) o[1] = s1;
+                    if (n + 1 < N) o[0] = (uint16_t)s01;
+                    if (n + 3 < N) o[1] = (uint16_t)(s01 >> 16);
                 }
             } else if (vec) {
                 if (OUT == 0) {
                     uint2 p;
-                    p.x = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
-                    p.y = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
+                    p.x = f32x2_to_bf16x2(y[0], y[1]);
+                    p.y = f32x2_to_bf16x2(y[2], y[3]);
                     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + idx) = p;
                 } else if (OUT == 1) {
                     *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + idx) = float4{y[0], y[1], y[2], y[3]};

@@ -91,12 +91,15 @@ __device__ __forceinline__ uint2 decode8(uint32_t x, uint4 t) {
     return r;
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+// fp32 -> bf16 bits, round to nearest even; a NaN keeps its sign and top payload bits and
+// becomes quiet ((u >> 16) | 0x40).  gfx950's v_cvt_pk_bf16_f32 does exactly this (checked
+// on every special class and a million random values, NaNs included), two values at once.
+typedef __bf16 w4a8_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float w4a8_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((w4a8_f32x2){lo, hi}, w4a8_bf16x2));
 }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)f32x2_to_bf16x2(f, 0.0f); }
 
 // Epilogue of one output: fp32(acc) * (xs * ws) [+ bias], each op rounded on its own.
 __device__ __forceinline__ float epilogue_f32(int32_t acc, float xs, float ws, const float* bias, int n) {

@@ -128,8 +128,10 @@ def test_rotate_quant_act_qmax_and_empty():
 
 # ------------------------------------------------------------- integer contraction
 
+# (256, 256, 256) and (513, 384, 1024): whole 256 x 128 tiles (their bf16 output goes through
+# LDS); (512, 260, 512): whole tiles with rows that are not 16-byte aligned (direct stores)
 GEMM_SHAPES = [(16, 256, 256), (37, 200, 768), (300, 1000, 512), (257, 129, 256), (1, 128, 4096),
-               (9, 64, 256), (513, 384, 1024), (64, 4096, 3072)]
+               (9, 64, 256), (513, 384, 1024), (64, 4096, 3072), (256, 256, 256), (512, 260, 512)]
 
 
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)

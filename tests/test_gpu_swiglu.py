@@ -77,6 +77,17 @@ def test_swiglu_epilogue_gemv_and_gemm(f, k, m):
             assert torch.equal(y_act.view(torch.int16), y_gemm.view(torch.int16)), "gemv_act != gemm"
 
 
+@pytest.mark.parametrize("f", [128, 132])
+def test_swiglu_whole_tiles(f):
+    # 256 rows: whole GEMM tiles; 2f = 256 output rows per pair-row give 16-byte aligned
+    # output rows (staged through LDS), 2f = 264 do not (direct stores)
+    layer, host = gate_up_layer(f, 256, synth.seed_for(19, 300, f), with_bias=True)
+    x = torch.from_numpy(synth.activations(256, 256, seed=synth.seed_for(19, 300, f + 1))).to(torch.bfloat16).to(DEV)
+    xq, xs = B.rotate_quant_act(x)
+    say("swiglu whole tiles", f)
+    check(B.w4a8_gemm(xq, xs, layer, B.SWIGLU), reference(xq, xs, host), f"gemm 256x{2 * f}x256")
+
+
 def test_swiglu_grouped_gemv_matches_single():
     items, singles = [], []
     for i, (f, k) in enumerate([(37, 256), (1536, 1024), (64, 512)] * 3):
