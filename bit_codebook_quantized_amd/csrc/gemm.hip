@@ -167,7 +167,12 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     cload(C2, min(2, last));
     aload(A0, 0);
     aload(A1, 1);
-    build_level_table(lut, codebook, tid, GM_THREADS);
+    {
+        float cb[16];   // uniform loads
+#pragma unroll
+        for (int c = 0; c < 16; ++c) cb[c] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(codebook[c])));
+        build_level_table_regs(lut, cb, tid, GM_THREADS);
+    }
     if (tid < BM) xs_t[tid] = m0 + tid < M ? xs[m0 + tid] : 0.0f;
     if (tid < BN) {
         ws_t[tid] = n0 + tid < N ? ws[n0 + tid] : 0.0f;
