@@ -33,6 +33,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int GI_THREADS = 512;
 constexpr int GI_BK = 128;          // output columns per block
@@ -178,6 +179,33 @@ __global__ __launch_bounds__(GI_THREADS) void grad_input_kernel(const uint16_t* 
     }
 
     // epilogue: lane holds D[k = 4 * c4 + r][m = r16] of each 16 x 16 tile
+    if (m0 + GI_BM <= M) {
+        // whole tile: each wave passes its 64 x 64 outputs through LDS (the operand buffers,
+        // free after the last barrier; 144-byte rows) and stores each row's 128 bytes with 8
+        // lanes, whole lines, as non-temporal stores (the output is not read again here)
+        constexpr int OP = 144;
+        uint8_t* ob = gi_smem + wave * (64 * OP);
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const f32x4 a = acc[ks][ms];
+                const bf16x2 lo = __builtin_convertvector((f32x2){a[0], a[1]}, bf16x2);
+                const bf16x2 hi = __builtin_convertvector((f32x2){a[2], a[3]}, bf16x2);
+                *reinterpret_cast<uint2*>(ob + (16 * ms + r16) * OP + 2 * (16 * ks + 4 * c4)) =
+                    uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+            }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = (lane >> 3) + 8 * i, c = lane & 7;
+            const uint4 v = *reinterpret_cast<const uint4*>(ob + row * OP + 16 * c);
+            const int64_t m = m0 + 64 * wm + row;
+            __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w},
+                                        reinterpret_cast<u32x4*>(out + m * K + k0 + 64 * wk + 8 * c));
+        }
+        return;
+    }
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms) {
         const int m = m0 + 64 * wm + 16 * ms + r16;
