@@ -92,6 +92,29 @@ __device__ __forceinline__ void store16(float* __restrict__ p, const float (&v)[
     for (int i = 0; i < 4; ++i) reinterpret_cast<float4*>(p)[i] = float4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
 }
 
+// Store a wave's 64 x 16 values, lane l holding elements 16l .. 16l + 15 of 1024 consecutive
+// floats at dst (elements at or past `valid` are not stored; valid is a multiple of 4).
+// The values are re-laid out through the wave's 4 KiB of LDS `buf` so that each store
+// instruction writes 1 KiB, not 16-byte pieces 64 bytes apart; chunk j of lane l sits at
+// chunk position j ^ ((l >> 2) & 3) of its 64 bytes, which keeps the writes and the reads
+// conflict-free.  The caller synchronises before (buf free) and this call synchronises
+// between the writes and the reads, so every thread of the block must call it.
+__device__ __forceinline__ void wave_store1024(float* __restrict__ dst, int64_t valid, const float (&w)[16],
+                                               float* buf) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(buf + 16 * lane + 4 * (j ^ ((lane >> 2) & 3))) =
+            float4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int src = 16 * i + (lane >> 2), j = lane & 3;   // the lane and chunk that hold it
+        const float4 v = *reinterpret_cast<const float4*>(buf + 16 * src + 4 * (j ^ ((src >> 2) & 3)));
+        if (256 * i + 4 * lane < valid) *reinterpret_cast<float4*>(dst + 256 * i + 4 * lane) = v;
+    }
+}
+
 // STOCH: stochastic rounding with the uniform draws u, else the nearest level (one path per
 // instantiation: with both in one kernel the compiler moved the level table to scratch).
 template <bool STOCH>
@@ -167,7 +190,7 @@ __global__ __launch_bounds__(RG_THREADS) void fake_quant_kernel(const float* __r
         (void)(asc ? nearest16_sorted(t, lvl, &lv) : nearest16_any(t, lvl, &lv));
         y[k] = __fmul_rn(lv, sch);
     }
-    store16(out + g * 16, y);
+    store16(out + g * 16, y);   // (a re-layout through LDS for whole-KiB stores measured no faster here)
 }
 
 __global__ __launch_bounds__(RG_THREADS) void dequant_kernel(const uint8_t* __restrict__ qpacked,
@@ -196,7 +219,9 @@ __global__ __launch_bounds__(RG_THREADS) void dequant_kernel(const uint8_t* __re
         for (int k = 0; k < 16; ++k) w[k] = 0.0f;
     }
     if (rotate_back) rotate16_in_place(w, slot, l16, tbuf, fbuf);   // block-uniform
-    if (ok) store16(out + row * K + col, w);
+    __syncthreads();   // the rotation buffer is free
+    const int wcol = c0 + (tid >> 6) * 1024;   // the wave's first column
+    wave_store1024(out + row * K + wcol, K - wcol, w, fbuf + (tid >> 6) * 1024);
 }
 
 // The dequantised, rotated-back weight plus a low-rank delta (one block per row chunk).
@@ -205,6 +230,9 @@ __global__ __launch_bounds__(RG_THREADS) void dequant_kernel(const uint8_t* __re
 // N / LM_ROWS times in all, from L2).  Thread t holds the deltas of columns
 // c0 + 16 t .. c0 + 16 t + 15 of each row in fp64; the B entries are block-uniform.
 constexpr int LM_THREADS = 128, LM_ROWS = 4, LM_CHUNK = LM_THREADS * 16;
+// the store re-layout (1024 floats per wave) reuses the rotation buffer
+static_assert((LM_THREADS / 16) * 16 * QTSTRIDE * sizeof(double) >= (LM_THREADS / 64) * 1024 * sizeof(float), "");
+static_assert(16 * 16 * QTSTRIDE * sizeof(double) >= (RG_THREADS / 64) * 1024 * sizeof(float), "");
 
 __global__ __launch_bounds__(LM_THREADS) void lora_merge_kernel(const uint8_t* __restrict__ qpacked,
                                                                 const uint8_t* __restrict__ srel,
@@ -290,11 +318,11 @@ __global__ __launch_bounds__(LM_THREADS) void lora_merge_kernel(const uint8_t* _
             for (int k = 0; k < 16; ++k) w[k] = 0.0f;
         }
         rotate16_in_place(w, slot, l16, tbuf, fbuf);   // all threads: back to the plain basis
-        if (ok) {
 #pragma unroll
-            for (int k = 0; k < 16; ++k) w[k] = __fadd_rn(w[k], (float)__dmul_rn(d[i][k], sc));
-            store16(out + row * K + col, w);
-        }
+        for (int k = 0; k < 16; ++k) w[k] = __fadd_rn(w[k], (float)__dmul_rn(d[i][k], sc));
+        const int wcol = c0 + (tid >> 6) * 1024;   // the wave's first column
+        wave_store1024(out + row * K + wcol, K - wcol, w, fbuf + (tid >> 6) * 1024);
+        __syncthreads();   // the store's reads of fbuf are done before the next rotation
     }
 }
 
