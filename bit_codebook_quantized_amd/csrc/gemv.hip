@@ -227,7 +227,7 @@ __device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds,
         if ((nch == 1 || !pass1) && ok) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                act[row * SLAB + act_chunk(16 * blk + i) * 16 + act_byte(l16)] = (uint8_t)quant1(r[i], inv, qmaxf);
+                act[row * SLAB + act_chunk(16 * blk + i) * 16 + act_byte(l16)] = quant1(r[i], inv, qmaxf);
         }
     };
 

@@ -41,11 +41,16 @@ template <int CH>
 __global__ __launch_bounds__(RQ_THREADS) void rotate_quant_kernel(const uint16_t* __restrict__ x, int64_t M, int K,
                                                                   int qmax, int8_t* __restrict__ xq,
                                                                   float* __restrict__ xs) {
-    __shared__ double tbuf[16 * 16 * TSTRIDE];
-    __shared__ __attribute__((aligned(16))) uint8_t qbuf[16 * 256];
+    // A slot's 16 lanes sit in one wave, and the slot uses only its own part of tbuf (the
+    // fp64 transposes, then the code transpose in its first 256 bytes), so those exchanges
+    // are ordered within the wave, with no block barrier; the row maximum is the one
+    // exchange between waves.  At 18.5 KB of LDS, 8 blocks share a CU.
+    __shared__ __attribute__((aligned(16))) double tbuf[16 * 16 * TSTRIDE];
+    static_assert(256 <= 16 * TSTRIDE * sizeof(double), "a slot's code transpose fits in its part of tbuf");
     __shared__ float smax[16];
 
     const int tid = threadIdx.x, slot = tid >> 4, l16 = tid & 15;
+    uint8_t* const qb = reinterpret_cast<uint8_t*>(tbuf + slot * 16 * TSTRIDE);
     const int nb = K >> 8;
     int rows_per_wg, row_local, blk0, nch;
     if (nb <= 16) {
@@ -65,7 +70,7 @@ __global__ __launch_bounds__(RQ_THREADS) void rotate_quant_kernel(const uint16_t
         for (int c = 0; c < KEEP; ++c) {
             if (c < nch) {
                 const int blk = blk0 + 16 * c;
-                rotate_block(x, row, K, blk, row_ok && blk < nb, slot, l16, tbuf, keep[c]);
+                rotate_block<true>(x, row, K, blk, row_ok && blk < nb, slot, l16, tbuf, keep[c]);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(keep[c][i]));
             }
@@ -74,7 +79,7 @@ __global__ __launch_bounds__(RQ_THREADS) void rotate_quant_kernel(const uint16_t
         for (int c = 0; c < nch; ++c) {
             const int blk = blk0 + 16 * c;
             float r[16];
-            rotate_block(x, row, K, blk, row_ok && blk < nb, slot, l16, tbuf, r);
+            rotate_block<true>(x, row, K, blk, row_ok && blk < nb, slot, l16, tbuf, r);
 #pragma unroll
             for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(r[i]));
         }
@@ -99,15 +104,15 @@ __global__ __launch_bounds__(RQ_THREADS) void rotate_quant_kernel(const uint16_t
         for (int c = 0; c < KEEP; ++c) {
             if (c < nch) {
                 const int blk = blk0 + 16 * c;
-                quant_store(keep[c], inv, qmaxf, row_ok && blk < nb, xq, row, K, blk, slot, l16, qbuf);
+                quant_store(keep[c], inv, qmaxf, row_ok && blk < nb, xq, row, K, blk, l16, qb);
             }
         }
     } else {
         for (int c = 0; c < nch; ++c) {
             const int blk = blk0 + 16 * c;
             float r[16];
-            rotate_block(x, row, K, blk, row_ok && blk < nb, slot, l16, tbuf, r);
-            quant_store(r, inv, qmaxf, row_ok && blk < nb, xq, row, K, blk, slot, l16, qbuf);
+            rotate_block<true>(x, row, K, blk, row_ok && blk < nb, slot, l16, tbuf, r);
+            quant_store(r, inv, qmaxf, row_ok && blk < nb, xq, row, K, blk, l16, qb);
         }
     }
 }

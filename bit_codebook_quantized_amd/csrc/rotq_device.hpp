@@ -28,11 +28,22 @@ namespace w4a8 {
 constexpr int TSTRIDE = 9;
 constexpr int ROTQ_TBUF_DOUBLES = 16 * 16 * TSTRIDE;   // one 16 x 8 tile per slot, 16 slots
 
+// Half of one stage: out_i / 2 = s / 2 - a_(3-i).  Halving is exact in fp64 for these
+// magnitudes, so four stages give the block product already divided by 16.
 __device__ __forceinline__ void radix4(double& a0, double& a1, double& a2, double& a3) {
     const double s = (a0 + a1) + (a2 + a3);
-    const double b0 = __builtin_fma(-2.0, a3, s), b1 = __builtin_fma(-2.0, a2, s);
-    const double b2 = __builtin_fma(-2.0, a1, s), b3 = __builtin_fma(-2.0, a0, s);
+    const double b0 = __builtin_fma(0.5, s, -a3), b1 = __builtin_fma(0.5, s, -a2);
+    const double b2 = __builtin_fma(0.5, s, -a1), b3 = __builtin_fma(0.5, s, -a0);
     a0 = b0; a1 = b1; a2 = b2; a3 = b3;
+}
+
+// Orders the LDS accesses of one wave: its LDS instructions execute in issue order, so a
+// lane's later read sees another lane's earlier write of the same wave once the compiler
+// keeps the program order (the fences), with no wait for the other waves.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // radix-16 over v[4*d1 + d0]: the stage of digit d0, then of digit d1
@@ -57,6 +68,7 @@ __device__ __forceinline__ RotIn rot_load(const uint16_t* __restrict__ x, int64_
 // Rotate one block from its loaded inputs.  Every thread of the block must call this
 // (it synchronises); threads with ok == false contribute zeros.  On return r[i] holds
 // the rotated value of column 16*i + l16 of the block, rounded to fp32.
+template <bool WAVE_SYNC = false>
 __device__ __forceinline__ void rotate_loaded(const RotIn in, bool ok, int slot, int l16, double* tbuf,
                                               float (&r)[16]) {
     double v[16];
@@ -74,26 +86,27 @@ __device__ __forceinline__ void rotate_loaded(const RotIn in, bool ok, int slot,
     for (int h = 0; h < 2; ++h) {   // columns 8h .. 8h + 7, read by lanes 8h .. 8h + 7
 #pragma unroll
         for (int i = 0; i < 8; ++i) t[l16 * TSTRIDE + i] = v[8 * h + i];
-        __syncthreads();
+        if constexpr (WAVE_SYNC) wave_lds_sync(); else __syncthreads();
         if ((l16 >> 3) == h) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) u[j] = t[j * TSTRIDE + (l16 & 7)];
         }
-        __syncthreads();
+        if constexpr (WAVE_SYNC) wave_lds_sync(); else __syncthreads();
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = u[j];
     radix16(v);     // digits 2, 3 (the lane index of the first half)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) r[i] = (float)(v[i] * 0.0625);
+    for (int i = 0; i < 16; ++i) r[i] = (float)v[i];
 }
 
 // Load and rotate block `blk` of row `row` (see rotate_loaded).
+template <bool WAVE_SYNC = false>
 __device__ __forceinline__ void rotate_block(const uint16_t* __restrict__ x, int64_t row, int K, int blk,
                                              bool ok, int slot, int l16, double* tbuf, float (&r)[16]) {
     RotIn in{};
     if (ok) in = rot_load(x, row, K, blk, l16);
-    rotate_loaded(in, ok, slot, l16, tbuf, r);
+    rotate_loaded<WAVE_SYNC>(in, ok, slot, l16, tbuf, r);
 }
 
 __device__ __forceinline__ float slot_max(float a) {
@@ -104,23 +117,29 @@ __device__ __forceinline__ float slot_max(float a) {
     return a;
 }
 
-__device__ __forceinline__ int8_t quant1(float v, double inv, float qmaxf) {
-    float q = __builtin_rintf((float)((double)v * inv));
-    q = __builtin_fminf(__builtin_fmaxf(q, -qmaxf), qmaxf);
-    return (int8_t)(int32_t)q;
+__device__ __forceinline__ uint8_t quant1(float v, double inv, float qmaxf) {
+    // Adding 1.5 * 2^23 rounds |x| < 2^22 to an integer half-to-even (the one fp32 add),
+    // and the sum's low byte is then that integer mod 256.  The clamp is applied to the
+    // sum (limits 1.5 * 2^23 -+ qmax, exact), so larger |x| (a subnormal row scale) end
+    // at -+qmax as well.
+    constexpr float MAGIC = 12582912.0f;   // 1.5 * 2^23
+    const float x = (float)((double)v * inv);
+    const float y = __builtin_amdgcn_fmed3f(x + MAGIC, MAGIC - qmaxf, MAGIC + qmaxf);
+    return (uint8_t)__float_as_uint(y);
 }
 
-// Quantise one rotated block held as r[i] = column 16*i + l16 and store it.
+// Quantise one rotated block held as r[i] = column 16*i + l16 and store it: the slot's
+// 16 lanes transpose the codes through their own 256 bytes of LDS, qb (16-byte aligned;
+// the slot's lanes are in one wave, so the accesses are ordered within the wave only).
 __device__ __forceinline__ void quant_store(const float (&r)[16], double inv, float qmaxf, bool ok,
                                             int8_t* __restrict__ xq, int64_t row, int K, int blk,
-                                            int slot, int l16, uint8_t* qbuf) {
-    uint8_t* qb = qbuf + slot * 256;
+                                            int l16, uint8_t* qb) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) qb[16 * i + l16] = (uint8_t)quant1(r[i], inv, qmaxf);
-    __syncthreads();
+    for (int i = 0; i < 16; ++i) qb[16 * i + l16] = quant1(r[i], inv, qmaxf);
+    wave_lds_sync();
     const uint4 out = *reinterpret_cast<const uint4*>(qb + 16 * l16);
     if (ok) *reinterpret_cast<uint4*>(xq + row * K + (int64_t)blk * 256 + 16 * l16) = out;
-    __syncthreads();
+    wave_lds_sync();
 }
 
 

@@ -126,6 +126,29 @@ def test_rotate_quant_act_qmax_and_empty():
     assert xq.shape == (0, 512)
 
 
+def test_rotate_quant_act_extreme_magnitudes():
+    # rows whose rotated values and scale are fp32 subnormals (a lone smallest bf16
+    # subnormal gives a scale a few dozen subnormal steps wide, so some quotients land
+    # well above qmax and only the clamp brings them back), and a row near the top of
+    # the range; every code and scale must still match the oracle
+    x = synth.activations(5, 1024, seed=79)
+    x[0] *= 1e-38
+    x[1] *= 3e-40
+    x[2] *= 1e36
+    x[3] = 0.0
+    x[3, 300] = 9.2e-41                 # rounds to the smallest bf16 subnormal, 2^-133
+    x[4] = 0.0
+    x[4, 5] = -9.2e-41
+    x[4, 700] = 3 * 9.2e-41
+    x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()   # the bf16 inputs both sides see
+    for qmax in (127, 7):
+        say("rotate_quant_act extreme magnitudes, qmax", qmax)
+        xq, xs = B.rotate_quant_act(bf16_dev(x), qmax=qmax)
+        rq, rs = O.rotate_quant_act(x, qmax=qmax)
+        assert np.array_equal(xs.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+        assert np.array_equal(xq.cpu().numpy(), rq)
+
+
 # ------------------------------------------------------------- integer contraction
 
 # (256, 256, 256) and (513, 384, 1024): whole 256 x 128 tiles (their bf16 output goes through
