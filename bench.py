@@ -148,20 +148,22 @@ def bench_prefill(args, torch, B, device):
 
 
 def timed_launches(torch, calls, n, sleep_cycles):
-    """Launch calls[i % len(calls)] n times with an event pair around each launch,
-    queued behind a GPU sleep long enough for the host to enqueue everything, so the
-    events time back-to-back GPU execution.  Returns the mean ms per launch."""
-    pairs = event_pairs(torch, n)
+    """Launch calls[i % len(calls)] n times back to back, queued behind a GPU sleep long
+    enough for the host to enqueue everything, with one event pair around the whole run
+    (an event between launches is a marker the next launch waits behind, which would add
+    a few us to every launch).  Returns the mean ms per launch, which includes the gaps
+    between consecutive kernels, and the host's enqueue time."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     torch.cuda._sleep(sleep_cycles)
+    e0.record()
     t0 = time.perf_counter()
     for i in range(n):
-        pairs[i][0].record()
         calls[i % len(calls)]()
-        pairs[i][1].record()
     enqueue_s = time.perf_counter() - t0
+    e1.record()
     torch.cuda.synchronize()
-    return mean_ms(pairs), enqueue_s
+    return e0.elapsed_time(e1) / n, enqueue_s
 
 
 def bench_gemv(args, torch, B, device):

@@ -42,8 +42,7 @@ __global__ __launch_bounds__(QZ_THREADS) void quantize_kernel(const float* __res
                                                               uint8_t* __restrict__ qpacked,
                                                               uint8_t* __restrict__ srel,
                                                               float* __restrict__ s_channel) {
-    __shared__ double tbuf[16 * 16 * QTSTRIDE];
-    float* const fbuf = reinterpret_cast<float*>(tbuf);   // reused after the fp64 transpose
+    __shared__ __attribute__((aligned(16))) double tbuf[16 * 16 * QTSTRIDE];
     __shared__ float wmax[QZ_THREADS / 64];
 
     const int tid = threadIdx.x, slot = tid >> 4, l16 = tid & 15, lane = tid & 63;
@@ -59,7 +58,7 @@ __global__ __launch_bounds__(QZ_THREADS) void quantize_kernel(const float* __res
     int q[16];
     float gs = 0.0f, rmax = 0.0f;
     for (int ch = 0; ch < nchunk; ++ch) {
-        load_group(wrow, K, ch * QZ_CHUNK, rotated != 0, slot, l16, tbuf, fbuf, w);
+        load_group(wrow, K, ch * QZ_CHUNK, rotated != 0, slot, l16, tbuf, w);
         gs = fit_group(w, cb, q, lv);
         if (ch * QZ_CHUNK + tid * 16 < K) {
 #pragma unroll
@@ -78,7 +77,7 @@ __global__ __launch_bounds__(QZ_THREADS) void quantize_kernel(const float* __res
     const int KH = K >> 1, G = K >> 4;
     for (int ch = nchunk - 1; ch >= 0; --ch) {
         if (ch != nchunk - 1) {
-            load_group(wrow, K, ch * QZ_CHUNK, rotated != 0, slot, l16, tbuf, fbuf, w);
+            load_group(wrow, K, ch * QZ_CHUNK, rotated != 0, slot, l16, tbuf, w);
             gs = fit_group(w, cb, q, lv);
         }
         const int col = ch * QZ_CHUNK + tid * 16;

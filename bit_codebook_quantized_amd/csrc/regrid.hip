@@ -97,23 +97,32 @@ __device__ __forceinline__ void store16(float* __restrict__ p, const float (&v)[
 // The values are re-laid out through the wave's 4 KiB of LDS `buf` so that each store
 // instruction writes 1 KiB, not 16-byte pieces 64 bytes apart; chunk j of lane l sits at
 // chunk position j ^ ((l >> 2) & 3) of its 64 bytes, which keeps the writes and the reads
-// conflict-free.  The caller synchronises before (buf free) and this call synchronises
-// between the writes and the reads, so every thread of the block must call it.
+// conflict-free.  buf is the wave's own (the 4 rotation slots of the wave, which it has
+// finished with), so the exchange is ordered within the wave: no block barrier.
 __device__ __forceinline__ void wave_store1024(float* __restrict__ dst, int64_t valid, const float (&w)[16],
                                                float* buf) {
     const int lane = threadIdx.x & 63;
+    wave_lds_sync();
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         *reinterpret_cast<float4*>(buf + 16 * lane + 4 * (j ^ ((lane >> 2) & 3))) =
             float4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int src = 16 * i + (lane >> 2), j = lane & 3;   // the lane and chunk that hold it
         const float4 v = *reinterpret_cast<const float4*>(buf + 16 * src + 4 * (j ^ ((src >> 2) & 3)));
         if (256 * i + 4 * lane < valid) *reinterpret_cast<float4*>(dst + 256 * i + 4 * lane) = v;
     }
+    wave_lds_sync();
 }
+
+// The wave's part of a rotation buffer (its 4 slots, 4608 bytes, 16-byte aligned): the
+// staging buffer of wave_store1024.
+__device__ __forceinline__ float* wave_region(double* tbuf) {
+    return reinterpret_cast<float*>(tbuf + (threadIdx.x >> 6) * 4 * 16 * QTSTRIDE);
+}
+static_assert(1024 * sizeof(float) <= 4 * 16 * QTSTRIDE * sizeof(double), "a wave's staging fits in its slots");
 
 // STOCH: stochastic rounding with the uniform draws u, else the nearest level (one path per
 // instantiation: with both in one kernel the compiler moved the level table to scratch).
@@ -124,13 +133,12 @@ __global__ __launch_bounds__(RG_THREADS) void requant_kernel(const float* __rest
                                                              const float* __restrict__ s_channel,
                                                              const float* __restrict__ u,
                                                              uint8_t* __restrict__ qpacked) {
-    __shared__ double tbuf[16 * 16 * QTSTRIDE];
-    float* const fbuf = reinterpret_cast<float*>(tbuf);   // reused after the fp64 transpose
+    __shared__ __attribute__((aligned(16))) double tbuf[16 * 16 * QTSTRIDE];
     const int tid = threadIdx.x, slot = tid >> 4, l16 = tid & 15;
     const int64_t row = blockIdx.x / nchunk;
     const int c0 = (blockIdx.x - (int)(row * nchunk)) * RG_CHUNK;
     float w[16];
-    load_group(wt + row * K, K, c0, rotated != 0, slot, l16, tbuf, fbuf, w);   // block-uniform
+    load_group(wt + row * K, K, c0, rotated != 0, slot, l16, tbuf, w);   // block-uniform
     const int col = c0 + tid * 16;
     if (col >= K) return;
     float cb[16];
@@ -198,8 +206,7 @@ __global__ __launch_bounds__(RG_THREADS) void dequant_kernel(const uint8_t* __re
                                                              const float* __restrict__ codebook,
                                                              const float* __restrict__ s_channel, int K, int nchunk,
                                                              int rotate_back, float* __restrict__ out) {
-    __shared__ double tbuf[16 * 16 * QTSTRIDE];
-    float* const fbuf = reinterpret_cast<float*>(tbuf);   // reused after the fp64 transpose
+    __shared__ __attribute__((aligned(16))) double tbuf[16 * 16 * QTSTRIDE];
     const int tid = threadIdx.x, slot = tid >> 4, l16 = tid & 15;
     const int64_t row = blockIdx.x / nchunk;
     const int c0 = (blockIdx.x - (int)(row * nchunk)) * RG_CHUNK;
@@ -218,10 +225,9 @@ __global__ __launch_bounds__(RG_THREADS) void dequant_kernel(const uint8_t* __re
 #pragma unroll
         for (int k = 0; k < 16; ++k) w[k] = 0.0f;
     }
-    if (rotate_back) rotate16_in_place(w, slot, l16, tbuf, fbuf);   // block-uniform
-    __syncthreads();   // the rotation buffer is free
+    if (rotate_back) rotate16_in_place(w, slot, l16, tbuf);   // block-uniform
     const int wcol = c0 + (tid >> 6) * 1024;   // the wave's first column
-    wave_store1024(out + row * K + wcol, K - wcol, w, fbuf + (tid >> 6) * 1024);
+    wave_store1024(out + row * K + wcol, K - wcol, w, wave_region(tbuf));
 }
 
 // The dequantised, rotated-back weight plus a low-rank delta (one block per row chunk).
@@ -230,9 +236,7 @@ __global__ __launch_bounds__(RG_THREADS) void dequant_kernel(const uint8_t* __re
 // N / LM_ROWS times in all, from L2).  Thread t holds the deltas of columns
 // c0 + 16 t .. c0 + 16 t + 15 of each row in fp64; the B entries are block-uniform.
 constexpr int LM_THREADS = 128, LM_ROWS = 4, LM_CHUNK = LM_THREADS * 16;
-// the store re-layout (1024 floats per wave) reuses the rotation buffer
-static_assert((LM_THREADS / 16) * 16 * QTSTRIDE * sizeof(double) >= (LM_THREADS / 64) * 1024 * sizeof(float), "");
-static_assert(16 * 16 * QTSTRIDE * sizeof(double) >= (RG_THREADS / 64) * 1024 * sizeof(float), "");
+static_assert(LM_THREADS % 64 == 0 && RG_THREADS % 64 == 0, "whole waves: each has its 4 rotation slots");
 
 __global__ __launch_bounds__(LM_THREADS) void lora_merge_kernel(const uint8_t* __restrict__ qpacked,
                                                                 const uint8_t* __restrict__ srel,
@@ -241,8 +245,7 @@ __global__ __launch_bounds__(LM_THREADS) void lora_merge_kernel(const uint8_t* _
                                                                 int K, int nchunk, const float* __restrict__ lora_a,
                                                                 const float* __restrict__ lora_b, int rank,
                                                                 float scale, float* __restrict__ out) {
-    __shared__ double tbuf[(LM_THREADS / 16) * 16 * QTSTRIDE];
-    float* const fbuf = reinterpret_cast<float*>(tbuf);   // reused after the fp64 transpose
+    __shared__ __attribute__((aligned(16))) double tbuf[(LM_THREADS / 16) * 16 * QTSTRIDE];
     const int tid = threadIdx.x, slot = tid >> 4, l16 = tid & 15;
     const int64_t row0 = (int64_t)(blockIdx.x / nchunk) * LM_ROWS;
     const int c0 = (int)(blockIdx.x % nchunk) * LM_CHUNK;
@@ -317,12 +320,11 @@ __global__ __launch_bounds__(LM_THREADS) void lora_merge_kernel(const uint8_t* _
 #pragma unroll
             for (int k = 0; k < 16; ++k) w[k] = 0.0f;
         }
-        rotate16_in_place(w, slot, l16, tbuf, fbuf);   // all threads: back to the plain basis
+        rotate16_in_place(w, slot, l16, tbuf);   // all threads: back to the plain basis
 #pragma unroll
         for (int k = 0; k < 16; ++k) w[k] = __fadd_rn(w[k], (float)__dmul_rn(d[i][k], sc));
         const int wcol = c0 + (tid >> 6) * 1024;   // the wave's first column
-        wave_store1024(out + row * K + wcol, K - wcol, w, fbuf + (tid >> 6) * 1024);
-        __syncthreads();   // the store's reads of fbuf are done before the next rotation
+        wave_store1024(out + row * K + wcol, K - wcol, w, wave_region(tbuf));
     }
 }
 

@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "w4a8_device.hpp"
+
 namespace w4a8 {
 
 // The 16 x 16 fp64 transpose of a slot goes through LDS in two halves of 8 columns, each
@@ -37,14 +39,6 @@ __device__ __forceinline__ void radix4(double& a0, double& a1, double& a2, doubl
     a0 = b0; a1 = b1; a2 = b2; a3 = b3;
 }
 
-// Orders the LDS accesses of one wave: its LDS instructions execute in issue order, so a
-// lane's later read sees another lane's earlier write of the same wave once the compiler
-// keeps the program order (the fences), with no wait for the other waves.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // radix-16 over v[4*d1 + d0]: the stage of digit d0, then of digit d1
 __device__ __forceinline__ void radix16(double (&v)[16]) {

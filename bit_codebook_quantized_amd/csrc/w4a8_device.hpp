@@ -91,6 +91,15 @@ __device__ __forceinline__ uint2 decode8(uint32_t x, uint4 t) {
     return r;
 }
 
+// Orders the LDS accesses of one wave: its LDS instructions execute in issue order, so a
+// lane's later read sees another lane's earlier write of the same wave once the compiler
+// keeps the program order (the fences), with no wait for the other waves.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // fp32 -> bf16 bits, round to nearest even; a NaN keeps its sign and top payload bits and
 // becomes quiet ((u >> 16) | 0x40).  gfx950's v_cvt_pk_bf16_f32 does exactly this (checked
 // on every special class and a million random values, NaNs included), two values at once.

@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "w4a8_device.hpp"
+
 namespace w4a8 {
 
 constexpr int QTSTRIDE = 9;      // padded row of the fp64 transpose buffer (16 x 8 halves)
@@ -170,11 +172,12 @@ __device__ __forceinline__ float fit_group(const float (&w)[16], const float (&c
 
 // Rotate the 16 fp32 values a thread holds -- columns 16*l16 .. 16*l16 + 15 of rotation
 // block `slot` -- in place: afterwards w[k] is the rotated value of the same column,
-// rounded once to fp32.  All threads of the block call it (it synchronises).  fbuf
-// (272 floats per slot) may alias tbuf (16 x QTSTRIDE doubles per slot): it is written
-// only after the barrier that ends the reads of tbuf.
-static_assert(16 * (256 + 16) * sizeof(float) <= 16 * 16 * QTSTRIDE * sizeof(double), "fbuf fits in tbuf");
-__device__ __forceinline__ void rotate16_in_place(float (&w)[16], int slot, int l16, double* tbuf, float* fbuf) {
+// rounded once to fp32.  A slot's 16 lanes sit in one wave and use only the slot's own
+// 16 x QTSTRIDE doubles of tbuf (the fp64 transpose, then the fp32 re-layout of 272
+// floats in the same bytes), so the exchanges are ordered within the wave and need no
+// block barrier; the slot's region must not be in use by other LDS work of the wave.
+static_assert((256 + 16) * sizeof(float) <= 16 * QTSTRIDE * sizeof(double), "the fp32 re-layout fits in a slot");
+__device__ __forceinline__ void rotate16_in_place(float (&w)[16], int slot, int l16, double* tbuf) {
     double v[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) v[k] = (double)w[k];
@@ -187,30 +190,30 @@ __device__ __forceinline__ void rotate16_in_place(float (&w)[16], int slot, int 
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) t[l16 * QTSTRIDE + i] = v[8 * h + i];
-        __syncthreads();
+        wave_lds_sync();
         if ((l16 >> 3) == h) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) u[j] = t[j * QTSTRIDE + (l16 & 7)];
         }
-        __syncthreads();
+        wave_lds_sync();
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = u[j];
     qradix16(v);   // digits 2, 3; v[i] is now column 16*i + l16 of the block
-    float* f = fbuf + slot * (256 + 16);
+    float* f = reinterpret_cast<float*>(t);
 #pragma unroll
     for (int i = 0; i < 16; ++i) f[i * 17 + l16] = (float)(v[i] * 0.0625);
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
     for (int k = 0; k < 16; ++k) w[k] = f[l16 * 17 + k];
-    __syncthreads();
+    wave_lds_sync();
 }
 
 // Load (and unless `rotated`, rotate) the 16 columns c0 + 16*tid .. of a row into w.
-// All threads call it (it synchronises).  Slot s of the block covers rotation block s
+// The 16 lanes of a slot call it together.  Slot s of the block covers rotation block s
 // of the chunk; blocks past the row's end contribute zeros and are never stored.
 __device__ __forceinline__ void load_group(const float* __restrict__ wrow, int K, int c0, bool rotated, int slot,
-                                           int l16, double* tbuf, float* fbuf, float (&w)[16]) {
+                                           int l16, double* tbuf, float (&w)[16]) {
     const int col = c0 + slot * 256 + l16 * 16;   // first column of this thread's 16
     const bool ok = col < K;
 #pragma unroll
@@ -218,7 +221,7 @@ __device__ __forceinline__ void load_group(const float* __restrict__ wrow, int K
         const float4 v = ok ? reinterpret_cast<const float4*>(wrow + col)[i] : float4{0.f, 0.f, 0.f, 0.f};
         w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
     }
-    if (!rotated) rotate16_in_place(w, slot, l16, tbuf, fbuf);
+    if (!rotated) rotate16_in_place(w, slot, l16, tbuf);
 }
 
 // Grid levels of one group ([AT] grid_levels): clamp(rint(fp32(cb[c] * s)), -127, 127),
