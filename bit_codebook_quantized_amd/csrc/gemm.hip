@@ -34,8 +34,9 @@
 // construction, and one decoded group is exactly one lane's weight operand.
 //
 // Tiles are mapped to blocks so that each of the 8 XCDs (blocks are dealt to XCDs round
-// robin) works on a contiguous range of tile ids, n fastest, which keeps one activation
-// row panel in its L2 for all the weight panels.
+// robin) works on a contiguous range of tile ids, and ids run over bands of 4 row tiles
+// (row tile fastest), so an XCD's range is a compact block of row x column tiles that
+// share activation and weight panels in its L2.
 #include "w4a8_device.hpp"
 
 namespace w4a8 {
@@ -68,7 +69,13 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     const int ntiles = tiles_m * tiles_n;
     int pid = blockIdx.x;
     if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);
-    const int tn = pid % tiles_n, tm = pid / tiles_n;
+    // tile ids run over bands of up to 4 row tiles, row tile fastest within a band, so a
+    // contiguous range of ids (one XCD's) covers a few row tiles x several column tiles
+    // instead of one row tile x every column tile: each XCD then reads 4 activation panels
+    // and 1/4 of the weight (at 2048 x 4096 x 4096) rather than 1 panel and all of it
+    const int band = pid / (4 * tiles_n), tm_first = 4 * band;
+    const int band_m = min(tiles_m - tm_first, 4), in_band = pid - band * 4 * tiles_n;
+    const int tm = tm_first + in_band % band_m, tn = in_band / band_m;
     const int m0 = tm * BM, n0 = tn * BN;
     const int nk = K / BK;   // even, because K % 256 == 0
 
