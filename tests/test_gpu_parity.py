@@ -152,9 +152,12 @@ def test_rotate_quant_act_extreme_magnitudes():
 # ------------------------------------------------------------- integer contraction
 
 # (256, 256, 256) and (513, 384, 1024): whole 256 x 128 tiles (their bf16 output goes through
-# LDS); (512, 260, 512): whole tiles with rows that are not 16-byte aligned (direct stores)
+# LDS); (512, 260, 512): whole tiles with rows that are not 16-byte aligned (direct stores);
+# (1300, 512, 256): 6 x 4 tiles, so the tile order has a band of 4 row tiles and a short
+# band of 2 (and 24 tiles take the XCD grouping)
 GEMM_SHAPES = [(16, 256, 256), (37, 200, 768), (300, 1000, 512), (257, 129, 256), (1, 128, 4096),
-               (9, 64, 256), (513, 384, 1024), (64, 4096, 3072), (256, 256, 256), (512, 260, 512)]
+               (9, 64, 256), (513, 384, 1024), (64, 4096, 3072), (256, 256, 256), (512, 260, 512),
+               (1300, 512, 256)]
 
 
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
