@@ -28,8 +28,10 @@ leave the precision open the oracle uses the readings listed in the design doc:
 
 Parity pins live in ``tests/test_oracle_*.py`` (closed forms, hand-worked
 values in ``tests/golden/``, library special cases, brute force on small
-tiles).  Parity unpinned: the optimality of ``FIXED_CODEBOOK`` and the quality
-gain of the ALS passes are taken from the page as given.
+tiles).  Parity unpinned: the optimality of ``FIXED_CODEBOOK`` is taken from the
+page as given (its levels are not the Lloyd-Max levels of any normal law to
+better than about 0.01, so it was presumably fitted to data).  The ALS passes
+are pinned by their normal equation and by the group error never rising.
 """
 
 from __future__ import annotations

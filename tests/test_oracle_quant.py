@@ -216,6 +216,24 @@ def test_als_step_solves_least_squares(seed):
         assert not np.array_equal(info[f"gs{it}"], info["gs0"])
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_als_passes_never_increase_the_group_error(seed):
+    # the quality gain of the refinement: a least-squares scale for fixed codes, then the
+    # nearest codes for that scale, so the group's squared error can only fall from the
+    # absmax fit (pass 0) through each pass (up to fp32 rounding of gs), and it does fall
+    w = _small_rotated(n=32, k=256, seed=100 + seed)
+    info = {}
+    O.convrot_w4a8._quantize_rows(w, O.FIXED_CODEBOOK, 16, internals=info)
+    gw = info["gw"].astype(np.float64)
+    err = []
+    for it in range(O.ALS_ITERS + 1):
+        lv = O.FIXED_CODEBOOK[info[f"q{it}"]].astype(np.float64)
+        err.append(((gw - info[f"gs{it}"].astype(np.float64) * lv) ** 2).sum(axis=-1))
+    for it in range(O.ALS_ITERS):
+        assert np.all(err[it + 1] <= err[it] * (1 + 1e-5) + 1e-30)
+    assert err[-1].mean() < 0.95 * err[0].mean()
+
+
 def test_channel_scale_maps_largest_level_to_127():
     # s_channel = max |cb[q]*gs| / 127, so the largest |cb[q]| * srel per row is 127
     # up to the fp8 rounding of srel (3 mantissa bits: within 1/16 relative)
