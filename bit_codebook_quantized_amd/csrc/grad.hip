@@ -19,8 +19,8 @@
 //     transposed, 16-byte chunks XOR-swizzled by k / 16 (conflict-free writes and reads);
 //   - one barrier per step: step s + 1's loads are issued before step s's matrix-core
 //     work and written to the other LDS buffers after it;
-//   - tiles are dealt to the 8 XCDs in contiguous ranges, m-major, so the blocks of an
-//     XCD share their grad rows in its L2;
+//   - tiles are dealt to the 8 XCDs in contiguous ranges of ids, and ids run over bands of
+//     2 m-tiles, so the blocks of an XCD share 2 grad panels and half the weight in its L2;
 //   - n past N is zero in both operands; rows past M are read clamped, not stored.
 #include <type_traits>
 
@@ -68,7 +68,12 @@ __global__ __launch_bounds__(GI_THREADS) void grad_input_kernel(const uint16_t* 
     // block b runs on XCD b % 8; XCD x takes the contiguous tile range x * tiles / 8 ..
     const int b = blockIdx.x;
     const int t = (tiles % 8 == 0) ? (b % 8) * (tiles / 8) + b / 8 : b;
-    const int k0 = (t % ktiles) * GI_BK, m0 = (t / ktiles) * GI_BM;
+    // ids run over bands of 2 m-tiles (m fastest within a band): an XCD's 32 tiles at
+    // M = 2048, K = 4096 are 2 m-tiles x 16 k-tiles, so it reads 2 grad panels and half of
+    // the weight instead of 1 panel and all of it
+    const int mtiles = tiles / ktiles, band = t / (2 * ktiles), band_m = min(mtiles - 2 * band, 2);
+    const int in_band = t - band * 2 * ktiles;
+    const int k0 = (in_band / band_m) * GI_BK, m0 = (2 * band + in_band % band_m) * GI_BM;
     const int KH = K >> 1, G = K >> 4;
     const int nsteps = (N + GI_BN - 1) / GI_BN;
     const int r16 = lane & 15, c4 = lane >> 4;    // fragment row and 8-element chunk
