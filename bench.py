@@ -16,7 +16,7 @@ Weights are seeded N(0, 0.02^2) fp32 draws, rotated and quantised on the GPU by
 quantize_w4 (timed over five calls and reported on its own: it is an offline step,
 not part of the layer); activations are seeded synthetic draws.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 400] [--warmup 10] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -44,7 +44,7 @@ def weight_bytes(n, k):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--gemv-launches", type=int, default=640)
     p.add_argument("--sleep-cycles", type=float, default=4e7,
@@ -117,14 +117,16 @@ def bench_prefill(args, torch, B, device):
 
     for _ in range(args.warmup):
         step()
-    # The GEMM's duration from events in the timed region: steps 1, 5, 9, ... bracket the
-    # whole step and steps 3, 7, 11, ... only rotate_quant_act, both from an event before
-    # it, so the difference of the two means is the GEMM's time on the stream; each event
-    # costs the GPU a few microseconds (a marker the next launch waits behind), which the
-    # difference cancels and which sampling keeps out of most steps.  Step 0 is skipped:
-    # its events include the host's first launch latency.
-    whole = {i: event_pairs(torch, 1)[0] for i in range(1, args.steps, 4)}
-    part = {i: event_pairs(torch, 1)[0] for i in range(3, args.steps, 4)}
+    # The GEMM's duration from events in the timed region: steps 1, 1 + P, 1 + 2P, ...
+    # bracket the whole step and steps 1 + P/2, 1 + 3P/2, ... only rotate_quant_act, both
+    # from an event before it, so the difference of the two means is the GEMM's time on the
+    # stream.  Each event costs the GPU a few microseconds (a marker the next launch waits
+    # behind): the difference cancels it, and sampling one step in P/2 keeps it out of the
+    # rest (P = 16, or 4 for short runs).  Step 0 is skipped: its events include the host's
+    # first launch latency.
+    period = 16 if args.steps >= 32 else 4
+    whole = {i: event_pairs(torch, 1)[0] for i in range(1, args.steps, period)}
+    part = {i: event_pairs(torch, 1)[0] for i in range(1 + period // 2, args.steps, period)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
