@@ -54,7 +54,11 @@ __global__ __launch_bounds__(RQ_THREADS) void rotate_quant_kernel(const uint16_t
     const int nb = K >> 8;
     int rows_per_wg, row_local, blk0, nch;
     if (nb <= 16) {
-        rows_per_wg = 16 / nb; row_local = slot / nb; blk0 = slot % nb; nch = 1;
+        // quotients of integers below 17 by nb <= 16 from the approximate reciprocal: the
+        // exact quotient plus 1/2 is at least 1/32 away from an integer, far above its error
+        const float rn = __builtin_amdgcn_rcpf((float)nb);
+        rows_per_wg = (int)(16.5f * rn); row_local = (int)(((float)slot + 0.5f) * rn);
+        blk0 = slot - row_local * nb; nch = 1;
     } else {
         rows_per_wg = 1; row_local = 0; blk0 = slot; nch = (nb + 15) >> 4;
     }

@@ -103,11 +103,20 @@ __device__ __forceinline__ void rotate_block(const uint16_t* __restrict__ x, int
     rotate_loaded<WAVE_SYNC>(in, ok, slot, l16, tbuf, r);
 }
 
+// v from another lane of the same 16-lane row (a DPP source modifier, no LDS)
+template <int CTRL>
+__device__ __forceinline__ float row_dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over a slot's 16 lanes (one DPP row; every lane active).  The row mirror pairs
+// lane i with i ^ 15, the half-row mirror with i ^ 7, the two quad permutes with i ^ 1 and
+// i ^ 2; together they reach all 16 lanes.
 __device__ __forceinline__ float slot_max(float a) {
-    a = __builtin_fmaxf(a, __shfl_xor(a, 8, 16));
-    a = __builtin_fmaxf(a, __shfl_xor(a, 4, 16));
-    a = __builtin_fmaxf(a, __shfl_xor(a, 2, 16));
-    a = __builtin_fmaxf(a, __shfl_xor(a, 1, 16));
+    a = __builtin_fmaxf(a, row_dpp<0x140>(a));   // row_mirror
+    a = __builtin_fmaxf(a, row_dpp<0x141>(a));   // row_half_mirror
+    a = __builtin_fmaxf(a, row_dpp<0xB1>(a));    // quad_perm [1, 0, 3, 2]
+    a = __builtin_fmaxf(a, row_dpp<0x4E>(a));    // quad_perm [2, 3, 0, 1]
     return a;
 }
 
