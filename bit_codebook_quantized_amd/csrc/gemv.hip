@@ -203,14 +203,16 @@ __device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds,
         const int cc = nch == 1 ? 0 : (pass1 ? c : c - nch);
         const int blk = slot + 16 * cc;
         const bool ok = blk < nb;
-        rotate_loaded(in, ok, slot, l16, tbuf, r);
+        rotate_loaded<true>(in, ok, slot, l16, tbuf, r);   // exchanges within each slot's wave
         if (pass1) {
             if (cc == 0) amax = 0.0f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(r[i]));
             if (cc == nch - 1) {
                 const float a = slot_max(amax);
-                float* sm = smax + 16 * (row & 1);   // alternate rows: no barrier before the next write
+                // alternate rows: every thread reads row r's maxima before it reaches row r + 1's
+                // barrier, and row r + 2 writes only after that barrier
+                float* sm = smax + 16 * (row & 1);
                 if (l16 == 0) sm[slot] = a;
                 __syncthreads();
                 float rmax = 0.0f;
