@@ -17,8 +17,9 @@
 //     partner lanes (rows 2p, 2p + 1) swap a code word, scale byte and channel scale so
 //     each converts a pair of rows x 8 columns to bf16 (v_cvt_pk_bf16_f32) and writes it
 //     transposed, 16-byte chunks XOR-swizzled by k / 16 (conflict-free writes and reads);
-//   - one barrier per step: step s + 1's loads are issued before step s's matrix-core
-//     work and written to the other LDS buffers after it;
+//   - one barrier per step: step s + 2's loads are issued first, and step s + 1's operands
+//     (loaded a step earlier) are decoded into the other LDS buffers beside step s's
+//     matrix-core work;
 //   - tiles are dealt to the 8 XCDs in contiguous ranges of ids, and ids run over bands of
 //     2 m-tiles, so the blocks of an XCD share 2 grad panels and half the weight in its L2;
 //   - n past N is zero in both operands; rows past M are read clamped, not stored.
@@ -164,24 +165,36 @@ __global__ __launch_bounds__(GI_THREADS) void grad_input_kernel(const uint16_t* 
         }
     };
 
-    // prologue: level table, step 0's operands in buffer 0
-    Stage st;
-    load(st, 0);
+    // prologue: level table, step 0's operands in buffer 0, step 1's loads in flight
+    Stage sa, sb;
+    load(sa, 0);
     float cbv[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) cbv[c] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(codebook[c])));
     build_level_table_regs(lut, cbv, tid, GI_THREADS);
     __syncthreads();
-    store(st, 0, 0);
+    store(sa, 0, 0);
+    load(sa, 1);
     __syncthreads();
 
-    for (int s = 0; s < nsteps; ++s) {
-        load(st, s + 1);
-        __builtin_amdgcn_sched_barrier(0);   // the next step's loads stay ahead of this step's work
+    // Step s: the loads of step s + 2 are issued first; then step s + 1's operands, loaded
+    // a whole step earlier, are decoded and written into the other buffer while step s's
+    // matrix-core work reads this one, so the two interleave; one barrier ends the step.
+    // Two named stages alternate (no register copies).  Past the end the loads re-read the
+    // last step and the writes are zeros (n >= N) that nobody reads.
+    auto step = [&](int s, Stage& cur, Stage& nxt) __attribute__((always_inline)) {
+        load(nxt, s + 2);
+        __builtin_amdgcn_sched_barrier(0);   // the loads stay ahead of this step's work
+        store(cur, s + 1, (s + 1) & 1);
         mma(s & 1);
-        store(st, s + 1, (s + 1) & 1);       // past the end: zeros (n >= N), never read
         __syncthreads();
+    };
+    int s = 0;
+    for (; s + 2 <= nsteps; s += 2) {
+        step(s, sa, sb);
+        step(s + 1, sb, sa);
     }
+    if (s < nsteps) step(s, sa, sb);
 
     // epilogue: lane holds D[k = 4 * c4 + r][m = r16] of each 16 x 16 tile
     if (m0 + GI_BM <= M) {
