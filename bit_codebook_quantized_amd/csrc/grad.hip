@@ -97,21 +97,24 @@ __global__ __launch_bounds__(GI_THREADS) void grad_input_kernel(const uint16_t* 
         st.s = srel[(int64_t)n * G + ((k0 + 16 * cg) >> 4)];
         st.sc = s_channel[n];
     };
-    // write step `step`'s operands into buffer `buf`
-    auto store = [&](const Stage& st, int step, int buf) __attribute__((always_inline)) {
+    // write step `step`'s operands into buffer `buf`; FULL: the whole step lies below N
+    // (every step but a ragged last one), so nothing is zeroed
+    auto store_as = [&](auto full, const Stage& st, int step, int buf) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full)::value;
         const int n0 = step * GI_BN;
         __bf16* gb = gt + buf * GI_GTILE;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int idx = tid + GI_THREADS * i, gr = idx >> 3, ch = idx & 7;
-            const uint4 v = n0 + 8 * ch < N ? st.g[i] : uint4{0u, 0u, 0u, 0u};   // N % 8 == 0
+            const uint4 v = FULL || n0 + 8 * ch < N ? st.g[i] : uint4{0u, 0u, 0u, 0u};   // N % 8 == 0
             *reinterpret_cast<uint4*>(gb + gr * GI_PITCH + 8 * ch) = v;
         }
-        // the partner row's code word for this lane's 8 columns, its scale byte and scale
+        // the partner row's code word for this lane's 8 columns, its scale byte and scale:
+        // lane l's partner is l ^ 8, in the same 16-lane row (a DPP rotate by 8, no LDS)
         const uint32_t mine = h ? st.q.y : st.q.x, give = h ? st.q.x : st.q.y;
-        const uint32_t other = (uint32_t)__shfl_xor((int)give, 8, 64);
-        const uint32_t os = (uint32_t)__shfl_xor((int)st.s, 8, 64);
-        const float osc = __shfl_xor(st.sc, 8, 64);
+        const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, 0x128, 0xF, 0xF, false);
+        const uint32_t os = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)st.s, 0x128, 0xF, 0xF, false);
+        const float osc = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(st.sc), 0x128, 0xF, 0xF, false));
         const uint32_t qw[2] = {h ? other : mine, h ? mine : other};     // rows 2p, 2p + 1
         const uint32_t sw[2] = {h ? os : st.s, h ? st.s : os};
         const float scw[2] = {h ? osc : st.sc, h ? st.sc : osc};
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(GI_THREADS) void grad_input_kernel(const uint16_t* 
             const uint4 tr = reinterpret_cast<const uint4*>(lut)[sw[i]];
             const uint2 d = decode8(qw[i], tr);
             const float sb = (float)(__bf16)scw[i];            // s_channel rounded to bf16
-            const bool ok = n0 + 2 * p + i < N;                 // rows past N: zero
+            const bool ok = FULL || n0 + 2 * p + i < N;        // rows past N: zero
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float w8 = (float)(int8_t)(uint8_t)((j < 4 ? d.x : d.y) >> (8 * (j & 3)));
@@ -136,6 +139,12 @@ __global__ __launch_bounds__(GI_THREADS) void grad_input_kernel(const uint16_t* 
             const bf16x2 pr = __builtin_convertvector((f32x2){v[0][j], v[1][j]}, bf16x2);
             *reinterpret_cast<bf16x2*>(wb + (16 * cg + 8 * h + j) * GI_PITCH) = pr;
         }
+    };
+    auto store = [&](const Stage& st, int step, int buf) __attribute__((always_inline)) {
+        if (step * GI_BN + GI_BN <= N)   // block-uniform
+            store_as(std::true_type{}, st, step, buf);
+        else
+            store_as(std::false_type{}, st, step, buf);
     };
 
     f32x4 acc[4][4];
