@@ -430,8 +430,16 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
                     v[i] = keep + __shfl_xor(send, o, 64);
                 }
             }
-#pragma unroll
-            for (int o = 32 >> L; o >= 1; o >>= 1) v[0] += __shfl_xor(v[0], o, 64);
+            // then the sum over the 64 >> L lanes that share a value: within a 16-lane row by
+            // DPP (quad xor 1 and xor 2, then the half-row mirror pairs quads, the row mirror
+            // pairs half-rows), across rows by lane shuffles; every lane ends with the sum
+            constexpr int G = 64 >> L;
+            if constexpr (G >= 2) v[0] += __builtin_amdgcn_update_dpp(0, v[0], 0xB1, 0xF, 0xF, false);
+            if constexpr (G >= 4) v[0] += __builtin_amdgcn_update_dpp(0, v[0], 0x4E, 0xF, 0xF, false);
+            if constexpr (G >= 8) v[0] += __builtin_amdgcn_update_dpp(0, v[0], 0x141, 0xF, 0xF, false);
+            if constexpr (G >= 16) v[0] += __builtin_amdgcn_update_dpp(0, v[0], 0x140, 0xF, 0xF, false);
+            if constexpr (G >= 32) v[0] += __shfl_xor(v[0], 16, 64);
+            if constexpr (G >= 64) v[0] += __shfl_xor(v[0], 32, 64);
 
             const int n0 = ((tile0 + t * tstride) * WAVES + wave) * R;
             const int idx = lane >> (6 - L);
