@@ -88,20 +88,6 @@ __device__ __forceinline__ uint4 act_merge(uint4 v) {   // inverse of act_split
 // byte position of column j (0..15) of a chunk
 __device__ __forceinline__ int act_byte(int j) { return (j & 8) | ((j & 1) << 2) | ((j >> 1) & 3); }
 
-// The 8 codes of one packed dword (byte i = code 2i | code 2i+1 << 4) against the
-// 16-level row t = {L0..3, L4..7, L8..11, L12..15}: .x = the levels of columns 0, 2, 4, 6,
-// .y = those of columns 1, 3, 5, 7.  `id` is 0x03020100 held in a register (so the merge
-// selector is one and-or).
-__device__ __forceinline__ uint2 decode_split(uint32_t x, uint4 t, uint32_t id) {
-    const uint32_t se = x & 0x07070707u;           // even codes, low 3 bits
-    const uint32_t so = (x >> 4) & 0x07070707u;    // odd codes, low 3 bits
-    const uint32_t lo_e = perm(t.y, t.x, se), hi_e = perm(t.w, t.z, se);
-    const uint32_t lo_o = perm(t.y, t.x, so), hi_o = perm(t.w, t.z, so);
-    // bit 3 of each code picks the upper half of the table: selector i or i + 4
-    const uint32_t me = ((x >> 1) & 0x04040404u) | id;
-    const uint32_t mo = ((x >> 5) & 0x04040404u) | id;
-    return uint2{perm(hi_e, lo_e, me), perm(hi_o, lo_o, mo)};
-}
 
 // Activation staging: MM rows x cols bytes of xq from column k0 (cols <= slab_cols(MM))
 // -> act[m * slab_cols(MM) ...].  Every load is issued before the first wait; `between`

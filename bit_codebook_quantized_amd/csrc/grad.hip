@@ -122,12 +122,12 @@ __global__ __launch_bounds__(GI_THREADS) void grad_input_kernel(const uint16_t* 
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const uint4 tr = reinterpret_cast<const uint4*>(lut)[sw[i]];
-            const uint2 d = decode8(qw[i], tr);
+            const uint2 d = decode_split(qw[i], tr, 0x03020100u);   // .x even, .y odd columns
             const float sb = (float)(__bf16)scw[i];            // s_channel rounded to bf16
             const bool ok = FULL || n0 + 2 * p + i < N;        // rows past N: zero
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float w8 = (float)(int8_t)(uint8_t)((j < 4 ? d.x : d.y) >> (8 * (j & 3)));
+                const float w8 = (float)(int8_t)(uint8_t)(((j & 1) ? d.y : d.x) >> (8 * (j >> 1)));
                 v[i][j] = ok ? __fmul_rn(w8, sb) : 0.0f;          // exact: 8 x 8 significant bits
             }
         }

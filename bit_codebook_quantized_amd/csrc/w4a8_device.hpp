@@ -91,6 +91,21 @@ __device__ __forceinline__ uint2 decode8(uint32_t x, uint4 t) {
     return r;
 }
 
+// The 8 codes of one packed dword (byte i = code 2i | code 2i+1 << 4) against the
+// 16-level row t = {L0..3, L4..7, L8..11, L12..15}: .x = the levels of columns 0, 2, 4, 6,
+// .y = those of columns 1, 3, 5, 7.  `id` is 0x03020100 held in a register (so the merge
+// selector is one and-or).
+__device__ __forceinline__ uint2 decode_split(uint32_t x, uint4 t, uint32_t id) {
+    const uint32_t se = x & 0x07070707u;           // even codes, low 3 bits
+    const uint32_t so = (x >> 4) & 0x07070707u;    // odd codes, low 3 bits
+    const uint32_t lo_e = perm(t.y, t.x, se), hi_e = perm(t.w, t.z, se);
+    const uint32_t lo_o = perm(t.y, t.x, so), hi_o = perm(t.w, t.z, so);
+    // bit 3 of each code picks the upper half of the table: selector i or i + 4
+    const uint32_t me = ((x >> 1) & 0x04040404u) | id;
+    const uint32_t mo = ((x >> 5) & 0x04040404u) | id;
+    return uint2{perm(hi_e, lo_e, me), perm(hi_o, lo_o, mo)};
+}
+
 // Orders the LDS accesses of one wave: its LDS instructions execute in issue order, so a
 // lane's later read sees another lane's earlier write of the same wave once the compiler
 // keeps the program order (the fences), with no wait for the other waves.
