@@ -71,6 +71,7 @@ __global__ __launch_bounds__(QZ_THREADS) void quantize_kernel(const float* __res
     __syncthreads();
     rmax = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
     const float sch = __builtin_fmaxf(__fdiv_rn(rmax, 127.0f), 1e-8f);
+    const double inv_sch = 1.0 / (double)sch;   // for div_by
     if (tid == 0) s_channel[row] = sch;
 
     // pass 2: scales, grid levels and final codes (the last chunk's fit is still held)
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(QZ_THREADS) void quantize_kernel(const float* __res
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
                 float dummy;
-                const uint32_t code = (uint32_t)nearest16(__fdiv_rn(w[k], sch), lvl, &dummy);
+                const uint32_t code = (uint32_t)nearest16(div_by(w[k], inv_sch), lvl, &dummy);
                 packed[k >> 3] |= code << (4 * (k & 7));
             }
             *reinterpret_cast<uint2*>(qpacked + row * KH + (col >> 1)) = uint2{packed[0], packed[1]};

@@ -145,6 +145,7 @@ __global__ __launch_bounds__(RG_THREADS) void requant_kernel(const float* __rest
 #pragma unroll
     for (int c = 0; c < 16; ++c) cb[c] = codebook[c];
     const float sch = s_channel[row];
+    const double inv_sch = 1.0 / (double)sch;   // for div_by
     float lvl[16];
     const float s = e4m3fn_to_f32(srel[row * (K >> 4) + (col >> 4)]);
     grid_levels16(cb, s, lvl);
@@ -155,18 +156,18 @@ __global__ __launch_bounds__(RG_THREADS) void requant_kernel(const float* __rest
     if constexpr (STOCH) {
 #pragma unroll
         for (int k = 0; k < 16; ++k)
-            packed[k >> 3] |= stochastic16(__fdiv_rn(w[k], sch), r[k], lvl) << (4 * (k & 7));
+            packed[k >> 3] |= stochastic16(div_by(w[k], inv_sch), r[k], lvl) << (4 * (k & 7));
     } else if (asc) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             float dummy;
-            packed[k >> 3] |= (uint32_t)nearest16_sorted(__fdiv_rn(w[k], sch), lvl, &dummy) << (4 * (k & 7));
+            packed[k >> 3] |= (uint32_t)nearest16_sorted(div_by(w[k], inv_sch), lvl, &dummy) << (4 * (k & 7));
         }
     } else {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             float dummy;
-            packed[k >> 3] |= (uint32_t)nearest16_any(__fdiv_rn(w[k], sch), lvl, &dummy) << (4 * (k & 7));
+            packed[k >> 3] |= (uint32_t)nearest16_any(div_by(w[k], inv_sch), lvl, &dummy) << (4 * (k & 7));
         }
     }
     *reinterpret_cast<uint2*>(qpacked + row * (K >> 1) + (col >> 1)) = uint2{packed[0], packed[1]};
@@ -189,12 +190,13 @@ __global__ __launch_bounds__(RG_THREADS) void fake_quant_kernel(const float* __r
     grid_levels16(cb, s, lvl);
     const bool asc = levels_ascend(cb, s);
     const float sch = s_channel[row];
+    const double inv_sch = 1.0 / (double)sch;   // for div_by
     float w[16], y[16];
     load16(w_rot + g * 16, w);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         float lv;
-        const float t = __fdiv_rn(w[k], sch);
+        const float t = div_by(w[k], inv_sch);
         (void)(asc ? nearest16_sorted(t, lvl, &lv) : nearest16_any(t, lvl, &lv));
         y[k] = __fmul_rn(lv, sch);
     }

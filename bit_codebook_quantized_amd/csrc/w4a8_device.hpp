@@ -106,6 +106,14 @@ __device__ __forceinline__ uint2 decode_split(uint32_t x, uint4 t, uint32_t id) 
     return uint2{perm(hi_e, lo_e, me), perm(hi_o, lo_o, mo)};
 }
 
+// fp32(x / s) for a divisor s > 0 used many times, with inv = fp64(1 / s): the fp64
+// product x * inv is within about 2^-52 (relative) of the quotient, while a quotient of
+// two fp32 numbers is either exactly an fp32 value or midpoint, or at least 2^-49
+// (relative) away from every midpoint (2^-48 in the subnormal range), so rounding the
+// product once to fp32 gives the IEEE quotient.  Three instructions instead of the
+// ten of a correctly rounded fp32 division.
+__device__ __forceinline__ float div_by(float x, double inv) { return (float)((double)x * inv); }
+
 // Orders the LDS accesses of one wave: its LDS instructions execute in issue order, so a
 // lane's later read sees another lane's earlier write of the same wave once the compiler
 // keeps the program order (the fences), with no wait for the other waves.

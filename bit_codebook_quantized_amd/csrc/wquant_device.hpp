@@ -153,8 +153,9 @@ __device__ __forceinline__ float fit_group(const float (&w)[16], const float (&c
 #pragma unroll
     for (int k = 0; k < 16; ++k) gs = __builtin_fmaxf(gs, __builtin_fabsf(w[k]));
     gs = __builtin_fmaxf(gs, tiny);
+    double inv_gs = 1.0 / (double)gs;   // for div_by
 #pragma unroll
-    for (int k = 0; k < 16; ++k) q[k] = nearest16(__fdiv_rn(w[k], gs), cb, &lv[k]);
+    for (int k = 0; k < 16; ++k) q[k] = nearest16(div_by(w[k], inv_gs), cb, &lv[k]);
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         double num = 0.0, den = 0.0;
@@ -164,8 +165,9 @@ __device__ __forceinline__ float fit_group(const float (&w)[16], const float (&c
             den += (double)__fmul_rn(lv[k], lv[k]);
         }
         gs = __builtin_fmaxf(__fdiv_rn((float)num, __builtin_fmaxf((float)den, tiny)), tiny);
+        inv_gs = 1.0 / (double)gs;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) q[k] = nearest16(__fdiv_rn(w[k], gs), cb, &lv[k]);
+        for (int k = 0; k < 16; ++k) q[k] = nearest16(div_by(w[k], inv_gs), cb, &lv[k]);
     }
     return gs;
 }
