@@ -258,6 +258,8 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     // ---- epilogue: accumulator (mt, nb) register r of lane l holds column
     // 16*nb + 4*(l/16) + r of row 32*wave + 16*mt + l%16
     const bool vec = m0 + BM <= M && n0 + BN <= N && (N & 3) == 0;
+    // (each wave uses only its own part of the buffers, which every wave finished reading
+    // at the loop's last barrier, so the exchanges are ordered within the wave)
     // bf16 and SwiGLU outputs of a whole tile (rows 16-byte aligned): each wave passes its
     // 16-row halves through LDS (the weight buffers, free after the last barrier; rows
     // padded by 16 bytes, so the narrow writes of 16 rows and the 16-byte reads along a row
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
                 *reinterpret_cast<uint32_t*>(ob + rl * OPITCH + nl) =
                     f32x2_to_bf16x2(swiglu_f32(y[0], y[1]), swiglu_f32(y[2], y[3]));
             }
-            __syncthreads();
+            wave_lds_sync();
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int row = (lane >> 3) + 8 * i, c = lane & 7;
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
                     v4u{v.x, v.y, v.z, v.w},
                     reinterpret_cast<v4u*>(reinterpret_cast<uint16_t*>(out) + m * (N >> 1) + (n0 >> 1) + 8 * c));
             }
-            __syncthreads();
+            wave_lds_sync();
         }
         return;
     }
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
                 *reinterpret_cast<uint2*>(ob + rl * OPITCH + 2 * nl) =
                     uint2{f32x2_to_bf16x2(y[0], y[1]), f32x2_to_bf16x2(y[2], y[3])};
             }
-            __syncthreads();
+            wave_lds_sync();
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = cq + 4 * i;
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
                 __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w},
                                             reinterpret_cast<v4u*>(reinterpret_cast<uint16_t*>(out) + m * N + n0 + 8 * rl));
             }
-            __syncthreads();
+            wave_lds_sync();
         }
         return;
     }

@@ -222,7 +222,7 @@ __global__ __launch_bounds__(GI_THREADS) void grad_input_kernel(const uint16_t* 
                 *reinterpret_cast<uint2*>(ob + (16 * ms + r16) * OP + 2 * (16 * ks + 4 * c4)) =
                     uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
             }
-        __syncthreads();
+        wave_lds_sync();   // the wave's own rows: ordered within the wave
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int row = (lane >> 3) + 8 * i, c = lane & 7;
