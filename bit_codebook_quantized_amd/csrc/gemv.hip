@@ -89,6 +89,26 @@ __device__ __forceinline__ uint4 act_merge(uint4 v) {   // inverse of act_split
 __device__ __forceinline__ int act_byte(int j) { return (j & 8) | ((j & 1) << 2) | ((j >> 1) & 3); }
 
 
+// The value of lane l ^ o (o a power of two, every lane active) without going through
+// LDS where gfx950 has a register path: the permlane swaps for 32 and 16 (each returns
+// this lane's value and its partner's, in an order set by the lane's half or row
+// parity), DPP for 8 (row rotate) and for 2 and 1 (quad permutes); 4 takes a swizzle.
+__device__ __forceinline__ int32_t lane_xor(int32_t v, int o) {
+    const int lane = (int)(threadIdx.x & 63);
+    if (o == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+        return (int32_t)(lane < 32 ? r[1] : r[0]);
+    }
+    if (o == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+        return (int32_t)((lane & 16) ? r[0] : r[1]);
+    }
+    if (o == 8) return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);   // row_ror:8
+    if (o == 4) return __builtin_amdgcn_ds_swizzle(v, 0x101F);                      // xor 4 in 32 lanes
+    if (o == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);    // quad [2, 3, 0, 1]
+    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);                // quad [1, 0, 3, 2]
+}
+
 // Activation staging: MM rows x cols bytes of xq from column k0 (cols <= slab_cols(MM))
 // -> act[m * slab_cols(MM) ...].  Every load is issued before the first wait; `between`
 // runs after the loads and before the stores (the GEMV issues its first weight batch
@@ -413,7 +433,7 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
                 for (int i = 0; i < half; ++i) {
                     const int32_t d = (v[i] ^ v[i + half]) & hm;
                     const int32_t keep = v[i] ^ d, send = v[i + half] ^ d;
-                    v[i] = keep + __shfl_xor(send, o, 64);
+                    v[i] = keep + lane_xor(send, o);
                 }
             }
             // then the sum over the 64 >> L lanes that share a value: within a 16-lane row by
@@ -424,8 +444,8 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
             if constexpr (G >= 4) v[0] += __builtin_amdgcn_update_dpp(0, v[0], 0x4E, 0xF, 0xF, false);
             if constexpr (G >= 8) v[0] += __builtin_amdgcn_update_dpp(0, v[0], 0x141, 0xF, 0xF, false);
             if constexpr (G >= 16) v[0] += __builtin_amdgcn_update_dpp(0, v[0], 0x140, 0xF, 0xF, false);
-            if constexpr (G >= 32) v[0] += __shfl_xor(v[0], 16, 64);
-            if constexpr (G >= 64) v[0] += __shfl_xor(v[0], 32, 64);
+            if constexpr (G >= 32) v[0] += lane_xor(v[0], 16);
+            if constexpr (G >= 64) v[0] += lane_xor(v[0], 32);
 
             const int n0 = ((tile0 + t * tstride) * WAVES + wave) * R;
             const int idx = lane >> (6 - L);
