@@ -131,7 +131,10 @@ hipError_t launch_rotate_quant(const uint16_t* x, int64_t M, int K, int qmax, in
     const int rows_per_wg = nb <= 16 ? 16 / nb : 1;
     const int nch = nb <= 16 ? 1 : (nb + 15) / 16;
     const int64_t grid = (M + rows_per_wg - 1) / rows_per_wg;
-    const dim3 g((unsigned)grid), b(RQ_THREADS);
+    // only the slots that hold a block of a row: when nb does not divide 16 (K = 3072:
+    // 12 slots) the rest would run the whole rotation on zeros
+    const int threads = nb <= 16 ? 16 * nb * rows_per_wg : RQ_THREADS;
+    const dim3 g((unsigned)grid), b((unsigned)threads);
     if (nch <= 1) hipLaunchKernelGGL(rotate_quant_kernel<1>, g, b, 0, stream, x, M, K, qmax, xq, xs);
     else if (nch <= 2) hipLaunchKernelGGL(rotate_quant_kernel<2>, g, b, 0, stream, x, M, K, qmax, xq, xs);
     else if (nch <= 4) hipLaunchKernelGGL(rotate_quant_kernel<4>, g, b, 0, stream, x, M, K, qmax, xq, xs);
