@@ -69,7 +69,8 @@ __global__ __launch_bounds__(QZ_THREADS) void quantize_kernel(const float* __res
     for (int o = 32; o >= 1; o >>= 1) rmax = __builtin_fmaxf(rmax, __shfl_xor(rmax, o, 64));
     if (lane == 0) wmax[tid >> 6] = rmax;
     __syncthreads();
-    rmax = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+    rmax = wmax[0];
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) rmax = __builtin_fmaxf(rmax, wmax[i]);   // uniform
     const float sch = __builtin_fmaxf(__fdiv_rn(rmax, 127.0f), 1e-8f);
     const double inv_sch = 1.0 / (double)sch;   // for div_by
     if (tid == 0) s_channel[row] = sch;
@@ -105,8 +106,12 @@ __global__ __launch_bounds__(QZ_THREADS) void quantize_kernel(const float* __res
 hipError_t launch_quantize(const float* w, int64_t N, int K, int rotated, const float* codebook, uint8_t* qpacked,
                            uint8_t* srel, float* s_channel, hipStream_t stream) {
     (void)hipGetLastError();   // clear a stale error so the check below is about this launch
-    hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)N), dim3(QZ_THREADS), 0, stream, w, K, rotated, codebook,
-                       qpacked, srel, s_channel);
+    // rows shorter than a chunk get only the waves that hold groups of the row (K = 3072:
+    // 3 waves; the fourth would fit zeros), whole waves so the lane reductions see no
+    // absent lanes
+    const int threads = K >= QZ_CHUNK ? QZ_THREADS : 64 * ((K / 16 + 63) / 64);
+    hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)N), dim3((unsigned)threads), 0, stream, w, K, rotated,
+                       codebook, qpacked, srel, s_channel);
     return hipGetLastError();
 }
 
