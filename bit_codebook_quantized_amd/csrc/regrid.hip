@@ -32,6 +32,10 @@ namespace {
 
 constexpr int RG_THREADS = 256;
 constexpr int RG_CHUNK = 4096;
+// threads per block of the nearest-level requantisation: a row shorter than a chunk gets
+// only the whole waves that hold its groups (K = 3072: 3 waves; the rest would rotate
+// zeros).  The stochastic form, which also reads the draws, measured slower that way.
+inline int rg_threads(int K) { return K >= RG_CHUNK ? RG_THREADS : 64 * ((K / 16 + 63) / 64); }
 
 // Stochastic bracket choice ([AT] _assign_grid, stochastic branch) among 16
 // non-decreasing levels; comparisons with a NaN level are false.
@@ -352,7 +356,7 @@ hipError_t launch_requantize(const float* w, int64_t N, int K, int rotated, cons
         hipLaunchKernelGGL(requant_kernel<true>, dim3((unsigned)(N * nchunk)), dim3(RG_THREADS), 0, stream, w, K,
                            nchunk, rotated, codebook, srel, s_channel, u, qpacked);
     else
-        hipLaunchKernelGGL(requant_kernel<false>, dim3((unsigned)(N * nchunk)), dim3(RG_THREADS), 0, stream, w, K,
+        hipLaunchKernelGGL(requant_kernel<false>, dim3((unsigned)(N * nchunk)), dim3((unsigned)rg_threads(K)), 0, stream, w, K,
                            nchunk, rotated, codebook, srel, s_channel, u, qpacked);
     return hipGetLastError();
 }
