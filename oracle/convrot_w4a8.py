@@ -20,15 +20,20 @@ quantizer's divisions and the epilogue; the oracle does those steps in numpy
 float32 (IEEE, round-to-nearest-even, no fused multiply-add).  Where the pages
 leave the precision open the oracle uses the readings listed in the design doc:
 
-  * rotation: the exact block product (fp64 here) rounded once to fp32;
+  * rotation: the exact block product rounded once to fp32 (fp64 where that
+    is provably exact, Python integers otherwise; a block with an infinite or
+    NaN input gives NaN);
+  * a row of activations without a finite maximum: scale NaN, codes 0;
   * quantizer sums (ALS): fp32 products added in fp64 in k order, then fp32;
   * int32 contraction: exact (fp64 BLAS is exact for these magnitudes, checked);
   * int32 -> fp32 and fp32 -> bf16 conversions: round-to-nearest-even;
   * a NaN decode product (an fp8 NaN scale byte) decodes to 0.
 
 Parity pins live in ``tests/test_oracle_*.py`` (closed forms, hand-worked
-values in ``tests/golden/``, library special cases, brute force on small
-tiles).  Parity unpinned: the optimality of ``FIXED_CODEBOOK`` is taken from the
+values in ``tests/golden/`` -- decodes, grid levels, a full quantiser trace
+through both ALS passes, an epilogue whose product order is visible --,
+library special cases, brute force on small tiles, exact rational checks of
+the scale steps and of the rotation).  Parity unpinned: the optimality of ``FIXED_CODEBOOK`` is taken from the
 page as given (its levels are not the Lloyd-Max levels of any normal law to
 better than about 0.01, so it was presumably fitted to data).  The ALS passes
 are pinned by their normal equation and by the group error never rising.
@@ -43,7 +48,8 @@ __all__ = [
     "ACT_QMAX", "e4m3fn_to_f32", "f32_to_e4m3fn", "f32_to_bf16_bits",
     "bf16_bits_to_f32", "hadamard", "rotate", "rotate_to_f32", "quant_act",
     "rotate_quant_act", "pack_codes", "unpack_codes", "decode_w4",
-    "assign_codes", "grid_levels", "assign_grid", "quantize_w4_rotated",
+    "assign_codes", "grid_levels", "assign_grid", "quantize_w4_rotated", "quantize_trace",
+    "nearest_level_index", "round_dyadic_to_f32",
     "quantize_w4", "gemm_exact", "epilogue", "linear", "dequantize",
     "assign_grid_stochastic", "requantize_codes", "fake_quant_rotated", "dequantize_f32",
     "ste_weight_bf16", "grad_input_exact", "interleave_rows", "swiglu_interleaved", "lora_delta",
@@ -150,9 +156,10 @@ def hadamard(size: int = ROT_BLOCK) -> np.ndarray:
 def rotate(x, block: int = ROT_BLOCK) -> np.ndarray:
     """[H3] fn rotate_activation: the last dimension is cut into consecutive
     blocks of ``block`` columns and each block (a row vector) is multiplied by
-    the normalised Hadamard matrix.  Computed in fp64 and returned in fp64;
-    the matrix is symmetric and its own inverse ([AT] dequantize_w4a8 relies
-    on applying it twice)."""
+    the normalised Hadamard matrix.  Computed in fp64 and returned in fp64 (a
+    quality reference; ``rotate_to_f32`` is the exact parity form).  The matrix
+    is symmetric and its own inverse ([AT] dequantize_w4a8 relies on applying
+    it twice)."""
     x = np.asarray(x, dtype=np.float64)
     if x.shape[-1] % block:
         raise ValueError(f"block {block} does not divide {x.shape}")
@@ -161,10 +168,85 @@ def rotate(x, block: int = ROT_BLOCK) -> np.ndarray:
     return y.reshape(x.shape)
 
 
+def round_dyadic_to_f32(num: int, exp2: int) -> np.float32:
+    """The fp32 value nearest to the exact number num * 2**exp2 (Python ints),
+    ties to the even significand, with fp32 subnormals (multiples of 2^-149)
+    and overflow to +-infinity (the IEEE rounding of an exact value)."""
+    if num == 0:
+        return F32(0.0)
+    neg, a = num < 0, abs(num)
+
+    def rne_shift(v: int, s: int) -> int:        # round v / 2^s to an integer, ties to even
+        if s <= 0:
+            return v << -s
+        q, r = v >> s, v & ((1 << s) - 1)
+        half = 1 << (s - 1)
+        return q + 1 if (r > half or (r == half and q & 1)) else q
+
+    top = a.bit_length() - 1 + exp2               # floor(log2 |value|)
+    if top >= -126:                               # normal range: 24 significant bits
+        s = a.bit_length() - 24
+        q = rne_shift(a, s)
+        e = exp2 + s
+        if q == 1 << 24:                          # the rounding carried into a new binade
+            q, e = q >> 1, e + 1
+        if q.bit_length() - 1 + e > 127:
+            return F32(-np.inf if neg else np.inf)
+    else:                                         # subnormal range: quantum 2^-149
+        q = rne_shift(a, -149 - exp2)
+        e = -149
+    val = float(q) * 2.0 ** e                     # exact: q < 2^25 and a power-of-two scale
+    return F32(-val if neg else val)
+
+
+def _f32_parts(x):
+    """Each fp32 value as (integer significand m, exponent e) with x = m * 2^e
+    (subnormals included, m = 0 for zeros); int64 arrays."""
+    u = np.asarray(x, dtype=F32).view(np.uint32).astype(np.int64)
+    ebits = (u >> 23) & 0xFF
+    frac = u & 0x7FFFFF
+    m = np.where(ebits > 0, frac | (1 << 23), frac)
+    e = np.where(ebits > 0, ebits - 150, -149)
+    m = np.where(u >> 31 == 1, -m, m)
+    return m, e
+
+
 def rotate_to_f32(x, block: int = ROT_BLOCK) -> np.ndarray:
-    """The rotated value rounded once to fp32 (reading: no intermediate
-    rounding; used for bf16 activations and for fp32 weights)."""
-    return rotate(x, block).astype(F32)
+    """The block product of fp32-valued inputs (bf16 activations, fp32 weights)
+    with the normalised Hadamard matrix, computed exactly and rounded once to
+    fp32 (reading: no intermediate rounding).  Entries are +-1/16 and the inputs
+    are dyadic, so a block's products all lie on the grid 2^(L - 4), L the
+    exponent of the lowest set significand bit among its non-zero inputs, and
+    every partial sum is below 16 * 2^(E + 1), E the exponent of its largest
+    input.  Whenever E - L <= 44 every partial sum therefore has at most 53
+    significant bits and the fp64 product (any summation order) is the exact
+    value, which is then rounded once; other blocks are summed with Python
+    integers and rounded by round_dyadic_to_f32.  A block holding an infinite
+    or NaN input has no finite product: all its outputs are NaN here."""
+    x = np.asarray(x, dtype=F32)
+    if x.shape[-1] % block:
+        raise ValueError(f"block {block} does not divide {x.shape}")
+    blocks = x.reshape(-1, block)
+    out = (blocks.astype(np.float64) @ hadamard(block)).astype(F32)
+    finite = np.isfinite(blocks).all(axis=1)
+    out[~finite] = np.nan
+    m, e = _f32_parts(np.where(np.isfinite(blocks), blocks, F32(0.0)))
+    nz = m != 0
+    lsb = e + np.where(nz, np.log2(np.where(nz, np.abs(m) & -np.abs(m), 1)).astype(np.int64), 0)
+    top = e + np.where(nz, np.floor(np.log2(np.where(nz, np.abs(m), 1))).astype(np.int64), 0)
+    big = np.where(nz, top, -10 ** 6).max(axis=1)
+    small = np.where(nz, lsb, 10 ** 6).min(axis=1)
+    wide = finite & nz.any(axis=1) & (big - small > 44)
+    if np.any(wide):
+        signs = np.sign(hadamard(block)).astype(np.int64)   # the +-1 pattern of H * sqrt(block)
+        shift = int(np.log2(np.sqrt(block)))                 # the 1/sqrt(block) = 2^-shift factor
+        for b in np.nonzero(wide)[0]:
+            base = int(e[b][nz[b]].min())
+            ints = [int(mi) << int(ei - base) for mi, ei in zip(m[b], e[b])]
+            for i in range(block):
+                total = sum(int(signs[i, j]) * ints[j] for j in range(block))
+                out[b, i] = round_dyadic_to_f32(total, base - shift)
+    return out.reshape(x.shape)
 
 
 # ----------------------------------------------------------------------------
@@ -174,12 +256,17 @@ def quant_act(v, qmax: int = ACT_QMAX):
     """[AT] w4a8_act_quant_kernel, per row of fp32 values: amax = max |v|;
     scale = amax / qmax in fp32 (1.0 for an all-zero row); q = v / scale in
     fp32, rounded half-to-even and clamped to [-qmax, qmax].  Returns
-    (int8 [M, K], fp32 [M])."""
+    (int8 [M, K], fp32 [M]).  A row holding an infinite or NaN value has no
+    usable scale (the page leaves it undefined); reading: its scale is NaN and
+    all its codes are 0, so every output of that row is NaN downstream."""
     v = np.asarray(v, dtype=F32)
+    bad = ~np.isfinite(v).all(axis=1)
+    v = np.where(bad[:, None], F32(0.0), v)
     amax = np.abs(v).max(axis=1)
     scale = np.where(amax > 0, amax / F32(qmax), F32(1.0)).astype(F32)
     q = np.rint((v / scale[:, None]).astype(F32))
     q = np.clip(q, -qmax, qmax)
+    scale = np.where(bad, F32(np.nan), scale).astype(F32)
     return q.astype(np.int8), scale
 
 
@@ -231,26 +318,33 @@ def decode_w4(packed, srel_u8, codebook, group: int = GROUP) -> np.ndarray:
 # weight quantiser  ([AT] _assign_codes, grid_levels, _assign_grid,
 # _quantize_rotated_rows, quantize_w4a8_rotated)
 
-def _nearest_of_sorted(target, lv_lo, lv_hi):
-    """Shared tie rule of [AT] _assign_codes / _assign_grid given the two
-    candidate levels: distances in fp32; the upper candidate only when it is
-    strictly closer."""
-    dlo = np.abs((target - lv_lo).astype(F32))
-    dhi = np.abs((target - lv_hi).astype(F32))
-    return dhi < dlo
+def nearest_level_index(values, levels) -> np.ndarray:
+    """The nearest-level rule of [AT] _assign_codes (against the codebook) and
+    _assign_grid, deterministic branch (against a group's int8-grid levels).
+    For each value, p = the number of levels strictly below it (for
+    non-decreasing levels, the left insertion point of a binary search); the
+    candidate indices are p - 1 and p, each clamped into the table; the one at p
+    wins only if its fp32 distance |value - level| is strictly smaller, so an
+    equal distance goes to the lower index.  values [..., n]; levels either [L]
+    (one table for all) or [..., L] with the same leading axes.  Returns the
+    chosen indices [..., n]."""
+    v = np.asarray(values, dtype=F32)
+    table = np.asarray(levels, dtype=F32)
+    if table.ndim == 1:
+        table = np.broadcast_to(table, v.shape[:-1] + table.shape)
+    size = table.shape[-1]
+    below = (table[..., None, :] < v[..., :, None]).sum(axis=-1)
+    cand_lo = np.clip(below - 1, 0, size - 1)
+    cand_hi = np.clip(below, 0, size - 1)
+    dist_lo = np.abs(v - np.take_along_axis(table, cand_lo, axis=-1))
+    dist_hi = np.abs(v - np.take_along_axis(table, cand_hi, axis=-1))
+    return np.where(dist_hi < dist_lo, cand_hi, cand_lo)
 
 
 def assign_codes(normalized, codebook) -> np.ndarray:
-    """[AT] _assign_codes: left insertion point p of each value in the sorted
-    codebook, candidates p-1 and p clamped to 0..15, the upper one only if it
-    is strictly closer."""
-    cb = np.asarray(codebook, dtype=F32)
-    x = np.asarray(normalized, dtype=F32)
-    last = cb.size - 1
-    pos = np.searchsorted(cb, x, side="left")
-    lo = np.clip(pos - 1, 0, last)
-    hi = np.clip(pos, 0, last)
-    return np.where(_nearest_of_sorted(x, cb[lo], cb[hi]), hi, lo)
+    """[AT] _assign_codes: the nearest codebook index of each group-normalised
+    weight (nearest_level_index against the sorted codebook)."""
+    return nearest_level_index(normalized, codebook)
 
 
 def grid_levels(codebook, srel_u8) -> np.ndarray:
@@ -263,19 +357,10 @@ def grid_levels(codebook, srel_u8) -> np.ndarray:
 
 
 def assign_grid(target, levels) -> np.ndarray:
-    """[AT] _assign_grid (deterministic branch): per group, left insertion
-    point of each target among the 16 non-decreasing levels (the count of
-    levels below it), candidates p-1 and p clamped, the upper one only if
-    strictly closer.  target [N, G, g], levels [N, G, 16] -> codes [N, G, g]."""
-    t = np.asarray(target, dtype=F32)
-    lv = np.asarray(levels, dtype=F32)
-    last = lv.shape[-1] - 1
-    pos = (lv[:, :, None, :] < t[:, :, :, None]).sum(axis=-1)
-    lo = np.clip(pos - 1, 0, last)
-    hi = np.clip(pos, 0, last)
-    lv_lo = np.take_along_axis(lv, lo.reshape(lv.shape[0], lv.shape[1], -1), axis=2).reshape(t.shape)
-    lv_hi = np.take_along_axis(lv, hi.reshape(lv.shape[0], lv.shape[1], -1), axis=2).reshape(t.shape)
-    return np.where(_nearest_of_sorted(t, lv_lo, lv_hi), hi, lo)
+    """[AT] _assign_grid, deterministic branch: the nearest of each group's 16
+    non-decreasing grid levels.  target [N, G, g], levels [N, G, 16] -> codes
+    [N, G, g]."""
+    return nearest_level_index(target, levels)
 
 
 def _sum_k_f64(a):
@@ -287,63 +372,72 @@ def _sum_k_f64(a):
     return acc.astype(F32)
 
 
-def _quantize_rows(w_rot, codebook, group, internals=None):
-    """[AT] _quantize_rotated_rows on one chunk of rows of the rotated fp32
-    weight:
-      1. group scale gs = max |w| over the group, at least 1e-8;
-      2. codes = nearest codebook level of w / gs;
-      3. twice: gs = sum(w * cb[q]) / max(sum(cb[q]^2), 1e-8), at least 1e-8,
-         then re-assign the codes;
-      4. channel scale = max over the row of |cb[q] * gs| / 127, at least 1e-8;
-      5. relative group scale = e4m3(gs / channel scale);
-      6. final codes = nearest int8-grid level (grid_levels) of w / channel scale.
-    Returns (packed u8 [n, K/2], srel u8 [n, G], s_channel fp32 [n]).  When
-    ``internals`` is a dict it receives the intermediate arrays (for tests)."""
-    n, k = w_rot.shape
-    groups = k // group
-    tiny = F32(1e-8)
-    cb = np.asarray(codebook, dtype=F32)
-    gw = np.asarray(w_rot, dtype=F32).reshape(n, groups, group)
-    gs = np.maximum(np.abs(gw).max(axis=-1, keepdims=True), tiny)
-    q = assign_codes((gw / gs).astype(F32), cb)
-    if internals is not None:
-        internals["gs0"], internals["q0"] = gs.copy(), q.copy()
-    for it in range(ALS_ITERS):
-        lv = cb[q]
-        num = _sum_k_f64((gw * lv).astype(F32))[..., None]
-        den = np.maximum(_sum_k_f64((lv * lv).astype(F32))[..., None], tiny)
-        if internals is not None:
-            internals[f"q_used{it + 1}"] = q.copy()
-        gs = np.maximum((num / den).astype(F32), tiny)
-        q = assign_codes((gw / gs).astype(F32), cb)
-        if internals is not None:
-            internals[f"gs{it + 1}"], internals[f"q{it + 1}"] = gs.copy(), q.copy()
-    shifted = (cb[q] * gs).astype(F32)
-    s_channel = np.maximum((np.abs(shifted).max(axis=(1, 2)) / F32(127.0)).astype(F32), tiny)
-    srel = f32_to_e4m3fn((gs[..., 0] / s_channel[:, None]).astype(F32))
-    target = (gw / s_channel[:, None, None]).astype(F32)
-    codes = assign_grid(target, grid_levels(cb, srel))
-    if internals is not None:
-        internals.update(gw=gw, gs=gs, q=q, s_channel=s_channel, srel=srel, target=target, codes=codes)
-    return pack_codes(codes.reshape(n, k)), srel, s_channel.astype(F32)
+TINY = F32(1e-8)   # [AT] the floor of every scale and denominator in the quantiser
 
 
-def quantize_w4_rotated(w_rot, codebook=None, group: int = GROUP, row_budget: int = 1 << 20):
+def _group_absmax_scale(groups):
+    """Step 1 of [AT] _quantize_rotated_rows: a group's first scale is its largest
+    |w|, floored at 1e-8.  groups [N, G, g] -> [N, G]."""
+    return np.maximum(np.abs(groups).max(axis=-1), TINY)
+
+
+def _als_scale(groups, chosen):
+    """One [AT] ALS pass (_ALS_ITERS of them): for the levels chosen so far, the
+    least-squares group scale sum(w * level) / sum(level^2), the denominator and
+    the result each floored at 1e-8.  Products in fp32, sums by _sum_k_f64, the
+    quotient an fp32 division.  groups, chosen [N, G, g] -> [N, G]."""
+    num = _sum_k_f64((groups * chosen).astype(F32))
+    den = np.maximum(_sum_k_f64((chosen * chosen).astype(F32)), TINY)
+    return np.maximum((num / den).astype(F32), TINY)
+
+
+def quantize_trace(w_rot, codebook=None, group: int = GROUP) -> dict:
+    """[AT] _quantize_rotated_rows applied to every row of the rotated fp32 weight
+    (rows are independent), returning every intermediate by name:
+      groups          the weight cut into groups of ``group`` columns, [N, G, g];
+      scale0, codes0  absmax group scale, nearest codebook index of w / scale;
+      scale<p>, codes<p> for p = 1 .. ALS_ITERS: the refined scale from the
+                      previous codes, and the nearest indices for it;
+      row_top         per row, the largest |codebook[code] * scale| (fp32 products);
+      s_channel       row_top / 127 in fp32, floored at 1e-8;
+      srel            e4m3 byte of scale / s_channel (fp32 quotient, RNE);
+      target          w / s_channel in fp32;
+      final_codes     nearest of the group's int8-grid levels (grid_levels) to
+                      the target, [N, G, g];
+      packed          final_codes packed two per byte."""
+    w = np.asarray(w_rot, dtype=F32)
+    n, k = w.shape
+    cb = FIXED_CODEBOOK if codebook is None else np.asarray(codebook, dtype=F32)
+    groups = w.reshape(n, k // group, group)
+    out = {"groups": groups}
+    scale = _group_absmax_scale(groups)
+    codes = assign_codes((groups / scale[..., None]).astype(F32), cb)
+    out["scale0"], out["codes0"] = scale, codes
+    for p in range(1, ALS_ITERS + 1):
+        scale = _als_scale(groups, cb[codes])
+        codes = assign_codes((groups / scale[..., None]).astype(F32), cb)
+        out[f"scale{p}"], out[f"codes{p}"] = scale, codes
+    row_top = np.abs((cb[codes] * scale[..., None]).astype(F32)).max(axis=(1, 2))
+    s_channel = np.maximum((row_top / F32(127.0)).astype(F32), TINY)
+    srel = f32_to_e4m3fn((scale / s_channel[:, None]).astype(F32))
+    target = (groups / s_channel[:, None, None]).astype(F32)
+    final = assign_grid(target, grid_levels(cb, srel))
+    out.update(row_top=row_top, s_channel=s_channel, srel=srel, target=target, final_codes=final,
+               packed=pack_codes(final.reshape(n, k)))
+    return out
+
+
+def quantize_w4_rotated(w_rot, codebook=None, group: int = GROUP):
     """[AT] quantize_w4a8_rotated: K must be a multiple of 16 and of the group
-    (ValueError otherwise); rows are independent and are processed in chunks
-    (memory only).  Returns (packed u8 [N, K/2], srel u8 [N, K/group],
+    (ValueError otherwise).  Returns (packed u8 [N, K/2], srel u8 [N, K/group],
     s_channel fp32 [N], codebook fp32 [16])."""
     w_rot = np.asarray(w_rot, dtype=F32)
-    n, k = w_rot.shape
+    k = w_rot.shape[1]
     if k % group or k % 16:
         raise ValueError(f"K={k} must be divisible by 16 and by group={group}")
     cb = FIXED_CODEBOOK if codebook is None else np.asarray(codebook, dtype=F32)
-    block = max(1, row_budget // max(k, 1))
-    parts = [_quantize_rows(w_rot[r0:r0 + block], cb, group) for r0 in range(0, n, block)]
-    packed = np.concatenate([p[0] for p in parts], axis=0)
-    srel = np.concatenate([p[1] for p in parts], axis=0)
-    sch = np.concatenate([p[2] for p in parts], axis=0)
-    return packed, srel, sch, cb
+    t = quantize_trace(w_rot, cb, group)
+    return t["packed"], t["srel"], t["s_channel"], cb
 
 
 def quantize_w4(w, codebook=None, block: int = ROT_BLOCK, group: int = GROUP):
