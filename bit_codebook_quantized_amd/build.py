@@ -24,6 +24,38 @@ HIPCC_FLAGS = [
 ]
 
 
+# Kernels whose main loop loads into registers with inline asm (the compiler sees those
+# registers as written at once): a spill of them would store stale data, so they must not
+# use scratch memory at all.
+NO_SCRATCH = {"gemm.hip": "gemm_kernel"}
+
+
+def check_no_scratch(hipcc: str) -> None:
+    """Compile each NO_SCRATCH source to gfx950 assembly and fail if a listed kernel
+    uses private (scratch) memory."""
+    import re
+    import tempfile
+    for src, kernel in NO_SCRATCH.items():
+        with tempfile.TemporaryDirectory() as td:
+            asm = os.path.join(td, "k.s")
+            cmd = [hipcc, *[f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")], "-S", "--cuda-device-only",
+                   "-o", asm, os.path.join(CSRC, src)]
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                raise RuntimeError(f"hipcc -S {src} failed:\n{res.stderr}")
+            text = open(asm).read()
+        found = 0
+        for block in text.split("  - .agpr_count:")[1:]:
+            name = re.search(r"\.name:\s+(\S+)", block)
+            priv = re.search(r"\.private_segment_fixed_size:\s+(\d+)", block)
+            if name and kernel in name.group(1):
+                found += 1
+                if priv is None or int(priv.group(1)) != 0:
+                    raise RuntimeError(f"{name.group(1)} uses scratch memory; its asm-loaded registers must not spill")
+        if not found:
+            raise RuntimeError(f"no {kernel} found in the assembly of {src}")
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source into libw4a8.so next to this file; returns its path."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -38,6 +70,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+    check_no_scratch(hipcc)
     os.replace(tmp, LIB)
     return LIB
 

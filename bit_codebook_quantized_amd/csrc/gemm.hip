@@ -8,35 +8,40 @@
 // decoded tile by tile into LDS here, so no int8 weight copy ever reaches HBM.
 //
 // Tiling.  A block of 512 threads (8 waves, two per SIMD) computes a 256 x 128 output
-// tile and steps K by 128 per iteration (two 64-deep MFMA half-steps).  Wave w owns the
-// 32 rows 32w..32w+31 and all 128 columns: 2 x 8 accumulators of
-// v_mfma_i32_16x16x64_i8.
-//  - Activations go straight from global memory into MFMA operand registers: no two
-//    waves share a row, so there is nothing to gain from LDS.  A lane loads 16
-//    consecutive k bytes of one row (16 rows x 64 B per load instruction).
-//  - The weight tile is decoded once per iteration into LDS and read by all 8 waves.
-//    Thread t loads 16 B of packed codes (two 16-column groups) of row t / 4 (16 rows x
-//    64 B per instruction, which the address unit serves at full rate), looks up the
-//    16 levels of each group's scale byte in the LDS level table, decodes with byte
-//    permutes and writes the 2 x 16 bytes where the MFMA fragment reads expect them.
-//  - Loads run ahead of use in register rings: activations two iterations, codes two
-//    and a half.
-//  - The decoded tile lives in three LDS buffers: iteration i multiplies buffer i % 3,
-//    while the tile of i + 2 is decoded into buffer (i + 2) % 3, one 16-column group in
-//    each half of the iteration, interleaved with the MFMAs.  The level-table rows a
-//    decode needs are read one half-iteration ahead.  One barrier per iteration, at its
-//    end.
-// MFMA operands are swapped (the weight fragment is the first operand) so that each lane
-// ends with 4 consecutive output columns of one row, stored as one vector.
+// tile in stages of 128 k.  Wave w owns rows 64 (w / 2) .. + 63 and columns 64 (w % 2)
+// .. + 63: 4 x 4 accumulators of v_mfma_i32_16x16x64_i8, both operands read from LDS.
 //
-// Both operands of an MFMA hold, in lane l, 16 consecutive k of row (or column) l % 16
-// from 16-column group l / 16 of the half-step, so they agree on the k order by
-// construction, and one decoded group is exactly one lane's weight operand.
+// Memory paths (all full 128-byte lines; 16-row x 64-byte patterns run at well under half
+// the L2-to-CU rate):
+//  - Activations go straight from global memory into LDS (global_load_lds_dwordx4): 32
+//    loads of 8 rows x 128 bytes per stage, no registers or vector instructions.  The
+//    16-byte chunks of a 128-byte row are XOR-swizzled by the row pair, so the MFMA
+//    fragment reads (16 rows, one chunk each) hit 16 distinct bank groups.
+//  - Packed codes come in two stages at a time (a 128-byte line per weight row): lane l
+//    of a load takes 16 bytes = two 16-column groups; the lanes of a row alternate which
+//    stage they hold between consecutive loads, so every lane decodes one piece per stage.
+//    Each piece is decoded with byte permutes against the LDS level-table row of its
+//    group's scale byte and written as two 16-byte fragments into the stage's weight
+//    buffer (same swizzle).
+//  - Pipeline: three activation buffers and three weight buffers.  Stage s multiplies
+//    buffer s % 3; the activations of s + 3 are requested and the weights of s + 2 are
+//    decoded meanwhile (half per MFMA half, interleaved with the MFMAs), and the codes of
+//    period (s + 4) / 2 are requested on even stages.  One barrier per stage, between the
+//    two MFMA halves: after it the first-half fragments of s + 1 are read while the
+//    second-half MFMAs of s run.
+//  - Every vector-memory instruction of the main loop is written as inline asm, so the
+//    compiler does not insert waits of its own; each wait below counts the instructions
+//    issued after the one it needs (vmcnt retires in issue order).  Code registers are
+//    passed through an empty asm after their wait, so no use can move above it.
+// MFMA operands are swapped (the weight fragment is the first operand) so that each lane
+// ends with 4 consecutive output columns of one row.
 //
 // Tiles are mapped to blocks so that each of the 8 XCDs (blocks are dealt to XCDs round
 // robin) works on a contiguous range of tile ids, and ids run over bands of 4 row tiles
 // (row tile fastest), so an XCD's range is a compact block of row x column tiles that
 // share activation and weight panels in its L2.
+#include <type_traits>
+
 #include "w4a8_device.hpp"
 
 namespace w4a8 {
@@ -46,14 +51,72 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr int GM_THREADS = 512;
-constexpr int BM = 256, BN = 128, BK = 128;   // K per iteration; MFMA K is 64
-constexpr int BUF_BYTES = BN * BK;           // one decoded weight tile, 16 KiB
+constexpr int WM = 4, WN = 2, NW = WM * WN;          // wave grid
+constexpr int BM = 256, BN = 128, BK = 128;          // block tile, k per stage
+constexpr int TM = BM / WM, TN = BN / WN, MT = TM / 16, NB = TN / 16;
+constexpr int A_STAGE = BM * BK;                     // 32 KiB of activations per stage
+constexpr int B_STAGE = BN * BK;                     // 16 KiB of decoded weights per stage
+constexpr int NBUF = 3;
+constexpr int AI = A_STAGE / 1024 / NW;              // activation loads per wave per stage
+constexpr int CI = 2 * BN * 128 / 1024 / NW / 2;     // code loads per wave per period (2 stages)
+constexpr int CV = 2 * CI;                           // + one scale load each
+static_assert(CI == 2, "one code piece per lane and stage");
 
-// Slot of a decoded 16-byte group in a buffer: [half h][column block nb][group c][column j],
-// with j XOR-swizzled so that both the writes (4 lanes per row, mixed h and c) and the
-// fragment reads (16 columns of one group) hit 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int bslot(int h, int nb, int c, int j) {
-    return ((h * 8 + nb) * 64 + c * 16 + (j ^ (4 * (2 * h + (c >> 1))))) * 16;
+// position of 16-byte chunk c (0..7) of 128-byte row r
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// The direct-to-LDS load takes its LDS address in m0.  The compiler reserves m0 but uses it
+// in none of these kernels (nothing else here needs it on gfx950: no LDS-to-register ops,
+// GWS or relative register indexing), so the asm sets it before each load.
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const int8_t*)p);
+}
+// 64 lanes x 16 bytes from sbase + voff into LDS at m0 + 16 * lane
+__device__ __forceinline__ void load_lds16(uint32_t voff, const void* sbase, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2" ::"v"(voff), "s"(m0), "s"(sbase)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ v4u load16(uint32_t voff, const void* sbase) {
+    v4u x;
+    asm volatile("global_load_dwordx4 %0, %1, %2" : "=v"(x) : "v"(voff), "s"(sbase));
+    return x;
+}
+__device__ __forceinline__ uint32_t load_u16(uint32_t voff, const void* sbase) {
+    uint32_t x;
+    asm volatile("global_load_ushort %0, %1, %2" : "=v"(x) : "v"(voff), "s"(sbase));
+    return x;
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
+}
+// at most N vector-memory instructions outstanding and all LDS operations done, then the
+// workgroup barrier (the memory clobber keeps LDS accesses on their side of it)
+template <int N>
+__device__ __forceinline__ void bar_wait() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+// the same for a uniform run-time count (only near the ends of the K loop); an unlisted
+// count waits for everything, which is always safe
+#define W4A8_CASES(F)                                                                                \
+    F(1) F(2) F(3) F(4) F(5) F(6) F(7) F(8) F(9) F(10) F(11) F(12) F(13) F(14) F(15) F(16) F(17) F(18) \
+        F(19) F(20)
+__device__ __forceinline__ void vm_wait_n(int n) {
+    switch (n) {
+#define W4A8_C(v) case v: vm_wait<v>(); break;
+        W4A8_CASES(W4A8_C)
+#undef W4A8_C
+        default: vm_wait<0>(); break;
+    }
+}
+__device__ __forceinline__ void bar_wait_n(int n) {
+    switch (n) {
+#define W4A8_C(v) case v: bar_wait<v>(); break;
+        W4A8_CASES(W4A8_C)
+#undef W4A8_C
+        default: bar_wait<0>(); break;
+    }
 }
 
 template <int OUT>
@@ -61,223 +124,302 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int M, const uint8_t* __restrict__ qp,
     const uint8_t* __restrict__ srel, const float* __restrict__ codebook, const float* __restrict__ ws,
     const float* __restrict__ bias, int N, int K, void* __restrict__ out, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) int8_t smem[NBUF * (A_STAGE + B_STAGE)];
     __shared__ __attribute__((aligned(16))) uint32_t lut[1024];
-    __shared__ __attribute__((aligned(16))) int8_t Bs[3][BUF_BYTES];
     __shared__ __attribute__((aligned(16))) float xs_t[BM], ws_t[BN], bias_t[BN];
+    int8_t* const As = smem;
+    int8_t* const Bs = smem + NBUF * A_STAGE;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / WN, wn = wave % WN;
     const int ntiles = tiles_m * tiles_n;
     int pid = blockIdx.x;
     if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);
-    // tile ids run over bands of up to 4 row tiles, row tile fastest within a band, so a
-    // contiguous range of ids (one XCD's) covers a few row tiles x several column tiles
-    // instead of one row tile x every column tile: each XCD then reads 4 activation panels
-    // and 1/4 of the weight (at 2048 x 4096 x 4096) rather than 1 panel and all of it
     const int band = pid / (4 * tiles_n), tm_first = 4 * band;
     const int band_m = min(tiles_m - tm_first, 4), in_band = pid - band * 4 * tiles_n;
     const int tm = tm_first + in_band % band_m, tn = in_band / band_m;
     const int m0 = tm * BM, n0 = tn * BN;
-    const int nk = K / BK;   // even, because K % 256 == 0
-
-    // ---- activation operand loads: lane holds row 32*wave + 16*mt + lane%16, 16 bytes
-    // at k = 128*i + 64*h + 16*(lane/16).  Rows past M read row M - 1: they only feed
-    // accumulators whose outputs are never stored.
-    const int8_t* a_ptr[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        const int m = min(m0 + 32 * wave + 16 * mt + (lane & 15), M - 1);
-        a_ptr[mt] = xq + (int64_t)m * K + (lane >> 4) * 16;
-    }
-    struct ASlot {   // one iteration: [h][mt]
-        v4i a00, a01, a10, a11;
-    };
-    auto aload = [&](ASlot& s, int i) __attribute__((always_inline)) {
-        const int k = i * BK;
-        s.a00 = *reinterpret_cast<const v4i*>(a_ptr[0] + k);
-        s.a01 = *reinterpret_cast<const v4i*>(a_ptr[1] + k);
-        s.a10 = *reinterpret_cast<const v4i*>(a_ptr[0] + k + 64);
-        s.a11 = *reinterpret_cast<const v4i*>(a_ptr[1] + k + 64);
-    };
-
-    // ---- weight code loads: thread owns row br = tid / 4 of the tile and the 32 codes
-    // at k = 128*i + 32*(tid%4): half bh = (tid%4)/2, groups bc, bc+1 of that half.
-    const int br = tid >> 2, bq = tid & 3, bh = bq >> 1, bc = 2 * (bq & 1);
+    const int NS = K / BK;   // even, because K % 256 == 0
+    const int NP = NS / 2;   // 256-deep code periods
     const int KH = K >> 1, G = K >> 4;
-    const int brow = min(n0 + br, N - 1);
-    const uint8_t* q_ptr = qp + (int64_t)brow * KH + bq * 16;
-    // the 4 scale bytes of half bh are one aligned dword; this thread uses bytes bc, bc+1
-    const uint8_t* s_ptr = srel + (int64_t)brow * G + bh * 4;
-    const int s_shift = 8 * bc;
-    struct CSlot {
-        v4u q;
-        uint32_t s;
+
+    // ---- activation loads: load j of a wave covers rows 8i .. 8i+7 (i = wave + 8j), lane
+    // (row 8i + lane/8, position lane%8), which holds chunk position ^ swz.  Rows past M read
+    // row M - 1: they only feed accumulators whose outputs are never stored.
+    const int8_t* a_base = xq + (int64_t)m0 * K;
+    uint32_t a_off[AI];
+#pragma unroll
+    for (int j = 0; j < AI; ++j) {
+        const int r = 8 * (wave + NW * j) + (lane >> 3);
+        a_off[j] = (uint32_t)(min(r, M - 1 - m0) * K + 16 * swz(r, lane & 7));
+    }
+    const uint32_t a_lds = __builtin_amdgcn_readfirstlane(lds_addr(As) + 1024 * wave);
+    auto issue_a = [&](int s, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < AI; ++j) load_lds16(a_off[j], a_base + s * BK, a_lds + buf * A_STAGE + 1024 * NW * j);
     };
-    auto cload = [&](CSlot& s, int i) __attribute__((always_inline)) {
-        s.q = *reinterpret_cast<const v4u*>(q_ptr + i * (BK / 2));
-        s.s = *reinterpret_cast<const uint32_t*>(s_ptr + i * (BK / 16));
+
+    // ---- code loads: load jj of a wave covers weight rows 8i .. 8i+7 (i = wave + 8jj) of a
+    // 256-deep period, lane (row 8i + lane/8, piece q = (lane%8) ^ 4(jj%2)); piece q holds the
+    // 32 codes of groups 2(q%4), 2(q%4)+1 of the period's stage q/4, and the u16 at 2q of the
+    // row's period scale bytes is their two scale bytes.  Rows past N read row N - 1.
+    const uint8_t* q_base = qp + (int64_t)n0 * KH;
+    const uint8_t* s_base = srel + (int64_t)n0 * G;
+    uint32_t q_off[CI], s_off[CI];
+#pragma unroll
+    for (int jj = 0; jj < CI; ++jj) {
+        const int n = min(8 * (wave + NW * jj) + (lane >> 3), N - 1 - n0), q = (lane & 7) ^ (4 * (jj & 1));
+        q_off[jj] = (uint32_t)(n * KH + 16 * q);
+        s_off[jj] = (uint32_t)(n * G + 2 * q);
+    }
+    struct Codes {
+        v4u q[CI];
+        uint32_t s[CI];
+    };
+    auto issue_codes = [&](Codes& c, int period) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jj = 0; jj < CI; ++jj) {
+            c.q[jj] = load16(q_off[jj], q_base + period * 128);
+            c.s[jj] = load_u16(s_off[jj], s_base + period * 16);
+        }
+    };
+    // the loads write the code registers asynchronously: after their wait, route the
+    // registers through an empty asm so that no use is scheduled before it
+    auto tie = [&](Codes& c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jj = 0; jj < CI; ++jj) asm volatile("" : "+v"(c.q[jj]), "+v"(c.s[jj]));
+    };
+    // the lane's piece of stage t (0/1) of a period: codes, level-table rows, weight row
+    const int hi = (lane >> 2) & 1, cpair = 2 * (lane & 3);
+    struct Piece {
+        v4u x;
+        int n;
+        uint4 t0, t1;
     };
     const uint4* lut4 = reinterpret_cast<const uint4*>(lut);
-    // level-table rows of the two groups (read one half ahead of their decode)
-    auto lut_row = [&](const CSlot& s, int g) __attribute__((always_inline)) {
-        return lut4[(s.s >> (s_shift + 8 * g)) & 0xFFu];
+    auto pick = [&](const Codes& c, int t) __attribute__((always_inline)) {
+        Piece p;
+        const bool second = (t ^ hi) != 0;
+        p.x.x = second ? c.q[1].x : c.q[0].x;
+        p.x.y = second ? c.q[1].y : c.q[0].y;
+        p.x.z = second ? c.q[1].z : c.q[0].z;
+        p.x.w = second ? c.q[1].w : c.q[0].w;
+        const uint32_t sc = second ? c.s[1] : c.s[0];
+        p.n = 8 * (wave + (second ? NW : 0)) + (lane >> 3);
+        p.t0 = lut4[sc & 0xFF];
+        p.t1 = lut4[(sc >> 8) & 0xFF];
+        return p;
     };
-    // decode group g of a code slot into buffer buf
-    int w_off[2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) w_off[g] = bslot(bh, br >> 4, bc + g, br & 15);
-    auto decode_store = [&](const CSlot& s, const uint4 t, int g, int buf) __attribute__((always_inline)) {
-        const uint2 d0 = decode8(g ? s.q.z : s.q.x, t), d1 = decode8(g ? s.q.w : s.q.y, t);
-        *reinterpret_cast<v4u*>(&Bs[buf][w_off[g]]) = v4u{d0.x, d0.y, d1.x, d1.y};
-    };
-
-    // ---- weight fragment reads: lane holds column 16*nb + lane%16, group lane/16 of half h
-    int r_off[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) r_off[h] = bslot(h, 0, lane >> 4, lane & 15);
-    struct BFrag {
-        v4i b0, b1, b2, b3, b4, b5, b6, b7;
-    };
-    auto bread = [&](BFrag& f, int buf, int h) __attribute__((always_inline)) {
-        const int8_t* p = &Bs[buf][r_off[h]];
-        f.b0 = *reinterpret_cast<const v4i*>(p + 0 * 1024);
-        f.b1 = *reinterpret_cast<const v4i*>(p + 1 * 1024);
-        f.b2 = *reinterpret_cast<const v4i*>(p + 2 * 1024);
-        f.b3 = *reinterpret_cast<const v4i*>(p + 3 * 1024);
-        f.b4 = *reinterpret_cast<const v4i*>(p + 4 * 1024);
-        f.b5 = *reinterpret_cast<const v4i*>(p + 5 * 1024);
-        f.b6 = *reinterpret_cast<const v4i*>(p + 6 * 1024);
-        f.b7 = *reinterpret_cast<const v4i*>(p + 7 * 1024);
+    // group g (0/1) of a piece: 16 codes -> 16 int8 levels, one fragment of the weight buffer
+    auto decode_group = [&](const Piece& p, int g, int buf) __attribute__((always_inline)) {
+        const uint2 d0 = decode8(g ? p.x.z : p.x.x, g ? p.t1 : p.t0);
+        const uint2 d1 = decode8(g ? p.x.w : p.x.y, g ? p.t1 : p.t0);
+        *reinterpret_cast<v4u*>(Bs + buf * B_STAGE + 128 * p.n + 16 * swz(p.n, cpair + g)) =
+            v4u{d0.x, d0.y, d1.x, d1.y};
     };
 
-    v4i acc[2][8];
+    // ---- fragments: lane l holds row (or column) l%16 of a 16-row slice, chunk 4h + l/16 of
+    // the stage (h = MFMA half); both operands agree on the k order by construction
+    int a_rd[MT], b_rd[NB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int mt = 0; mt < MT; ++mt) a_rd[mt] = 128 * (wm * TM + 16 * mt + (lane & 15));
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-    auto mfma_half = [&](const BFrag& f, const v4i& x0, const v4i& x1) __attribute__((always_inline)) {
-        const v4i b[8] = {f.b0, f.b1, f.b2, f.b3, f.b4, f.b5, f.b6, f.b7};
+    for (int nb = 0; nb < NB; ++nb) b_rd[nb] = 128 * (wn * TN + 16 * nb + (lane & 15));
+    const int rsw = ((lane & 15) >> 1) & 7;   // swz of those rows: their 16-aligned base adds 0
+    struct Frag {
+        v4i a[MT], b[NB];
+    };
+    auto read_frags = [&](Frag& f, int buf, int h) __attribute__((always_inline)) {
+        const int pos = 16 * ((4 * h + (lane >> 4)) ^ rsw);
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-            acc[0][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b[nb], x0, acc[0][nb], 0, 0, 0);
-            acc[1][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b[nb], x1, acc[1][nb], 0, 0, 0);
+        for (int mt = 0; mt < MT; ++mt) f.a[mt] = *reinterpret_cast<const v4i*>(As + buf * A_STAGE + pos + a_rd[mt]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) f.b[nb] = *reinterpret_cast<const v4i*>(Bs + buf * B_STAGE + pos + b_rd[nb]);
+    };
+    v4i acc[MT][NB];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    auto mfmas = [&](const Frag& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                acc[mt][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.b[nb], f.a[mt], acc[mt][nb], 0, 0, 0);
+    };
+    // issue order of an MFMA half: each MFMA followed by a share of the fragment reads, the
+    // decode's vector instructions and its LDS writes
+    auto interleave = [&]() __attribute__((always_inline)) {
+        constexpr int NMF = MT * NB, NRD = MT + NB;
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                             // MFMA
+            if (i * NRD / NMF != (i + 1) * NRD / NMF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                                             // VALU
+            if (i == NMF - 1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                          // LDS write
         }
     };
 
-    // ---- prologue: rings filled, level table and epilogue operands staged, iterations
-    // 0 and 1 decoded, the table rows of iteration 2 and the first-half fragments of
-    // iteration 0 read
-    ASlot A0, A1, A2;
-    CSlot C0, C1, C2;
-    const int last = nk - 1;
-    cload(C0, 0);
-    cload(C1, 1);
-    cload(C2, min(2, last));
-    aload(A0, 0);
-    aload(A1, 1);
+    // ---- epilogue operands (needed after the loop; the compiler waits for them there)
+    constexpr int EV = (BM + 2 * BN + GM_THREADS - 1) / GM_THREADS;
+    float ev[EV];
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+        const int i = tid + GM_THREADS * e;
+        float v = 0.0f;
+        if (i < BM) v = m0 + i < M ? xs[m0 + i] : 0.0f;
+        else if (i < BM + BN) v = n0 + i - BM < N ? ws[n0 + i - BM] : 0.0f;
+        else if (i < BM + 2 * BN) v = (bias && n0 + i - BM - BN < N) ? bias[n0 + i - BM - BN] : 0.0f;
+        ev[e] = v;
+    }
+
+    // ---- prologue.  Issue order: codes of period 0, A(0), codes of period 1, A(1), A(2);
+    // then stage t issues A(t + 3) and, when t is even, the codes of period (t + 4) / 2.
+    // ops_at(t) counts stage t's vector-memory instructions; every wait counts the
+    // instructions issued after the one it needs.
+    auto ops_at = [&](int t) __attribute__((always_inline)) {
+        return (t + 3 < NS ? AI : 0) + ((!(t & 1) && (t + 4) / 2 < NP) ? CV : 0);
+    };
+    Codes C0, C1;
+    issue_codes(C0, 0);
+    issue_a(0, 0);
+    if (NP > 1) issue_codes(C1, 1);
+    if (NS > 1) issue_a(1, 1);
+    if (NS > 2) issue_a(2, 2);
+    const int after_a1 = NS > 2 ? AI : 0;
+    const int after_p1 = (NS > 1 ? AI : 0) + after_a1;
+    const int after_a0 = (NP > 1 ? CV : 0) + after_p1;
     {
         float cb[16];   // uniform loads
 #pragma unroll
         for (int c = 0; c < 16; ++c) cb[c] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(codebook[c])));
         build_level_table_regs(lut, cb, tid, GM_THREADS);
     }
-    if (tid < BM) xs_t[tid] = m0 + tid < M ? xs[m0 + tid] : 0.0f;
-    if (tid < BN) {
-        ws_t[tid] = n0 + tid < N ? ws[n0 + tid] : 0.0f;
-        bias_t[tid] = (bias && n0 + tid < N) ? bias[n0 + tid] : 0.0f;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // level table
+    vm_wait_n(AI + after_a0);
+    tie(C0);
+    {
+        const Piece p0 = pick(C0, 0);
+        decode_group(p0, 0, 0);
+        decode_group(p0, 1, 0);
+        if (NS > 1) {
+            const Piece p1 = pick(C0, 1);
+            decode_group(p1, 0, 1);
+            decode_group(p1, 1, 1);
+        }
     }
-    __syncthreads();
-    decode_store(C0, lut_row(C0, 0), 0, 0);
-    decode_store(C0, lut_row(C0, 1), 1, 0);
-    decode_store(C1, lut_row(C1, 0), 0, 1);
-    decode_store(C1, lut_row(C1, 1), 1, 1);
-    cload(C0, min(3, last));
-    cload(C1, min(4, last));
-    uint4 T0 = lut_row(C2, 0), T1 = lut_row(C2, 1);
-    __syncthreads();
-    BFrag F0, F1;
-    bread(F0, 0, 0);
+    Piece pc;   // the piece of B(s + 2) during stage s
+    if (NS > 2) {
+        vm_wait_n(after_p1);
+        tie(C1);
+        pc = pick(C1, 0);
+    }
+    bar_wait_n(after_a0);   // B(0), B(1) written, A(0) landed
+    Frag F0, F1;
+    read_frags(F0, 0, 0);
 
-    // Iteration i, with a = activations of i, a_next = the slot to refill with i + 2,
-    // c = codes of i + 2 (their table rows T0, T1 already read), c_next = codes of i + 3:
-    //   first half : read the second-half fragments of i (buffer rd), refill a_next,
-    //                16 MFMAs on the first half interleaved with the decode of group 0
-    //                of c into buffer wr, then read c_next's first table row
-    //   second half: read the first-half fragments of i + 1 (buffer rd_next), 16 MFMAs
-    //                on the second half interleaved with the decode of group 1 of c,
-    //                then read c_next's second table row and refill c with i + 5
-    //   barrier    : buffer wr is complete for everyone, and buffer rd is free to be
-    //                overwritten by the next iteration
-    // Past the end, loads re-read the last iteration and decodes write a buffer nobody
-    // reads, so the loop body has no branches.
-    auto iter = [&](int i, const int rd, const int rd_next, const int wr, ASlot& a, ASlot& a_next, CSlot& c,
-                    CSlot& c_next) __attribute__((always_inline)) {
+    int buf = 0;   // s % 3
+    // steady: 4 <= s <= NS - 5, where every stage around s issues all its loads, so the wait
+    // counts are constants
+    auto stage = [&](int s, Codes& nxt, Codes& ld, auto steady_c) __attribute__((always_inline)) {
+        constexpr bool steady = decltype(steady_c)::value;
+        const int nbuf = buf == 2 ? 0 : buf + 1, dbuf = nbuf == 2 ? 0 : nbuf + 1;
+        const bool dec_on = steady || s + 2 < NS;
+        // first half: MFMAs of s, second-half fragments of s, first group of B(s + 2)
+        mfmas(F0);
+        read_frags(F1, buf, 1);
+        if (dec_on) decode_group(pc, 0, dbuf);
+        interleave();
         __builtin_amdgcn_sched_barrier(0);
-        bread(F1, rd, 1);
-        aload(a_next, min(i + 2, last));
-        mfma_half(F0, a.a00, a.a01);
-        decode_store(c, T0, 0, wr);
-        T0 = lut_row(c_next, 0);
-        // issue order: each MFMA followed by a share of the fragment reads, loads and
-        // decode, so the memory pipelines see a steady stream instead of bursts
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
-            if (k % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // fragment read
-            if (k % 4 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // activation load
-            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);                  // decode
+        // B(s + 1) complete, A(s + 1) landed (issued at stage s - 2), F1(s) read by every wave
+        if (steady) {
+            bar_wait<AI + CV>();
+        } else {
+            int after = 0;
+            if (s + 1 < NS) {
+                if (s == 0) after = after_a1;
+                else if (s == 1) after = ops_at(0);
+                else after = ((!(s & 1) && (s + 2) / 2 < NP) ? CV : 0) + ops_at(s - 1);
+            }
+            bar_wait_n(after);
         }
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // decoded group
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // next table row
+        if (steady || s + 3 < NS) issue_a(s + 3, buf);
+        if (!(s & 1) && (steady || (s + 4) / 2 < NP)) issue_codes(ld, (s + 4) / 2);
+        // second half: MFMAs of s, first-half fragments of s + 1, second group of B(s + 2)
+        mfmas(F1);
+        if (steady || s + 1 < NS) read_frags(F0, nbuf, 0);
+        if (dec_on) decode_group(pc, 1, dbuf);
+        interleave();
         __builtin_amdgcn_sched_barrier(0);
-        bread(F0, rd_next, 0);
-        mfma_half(F1, a.a10, a.a11);
-        decode_store(c, T1, 1, wr);
-        T1 = lut_row(c_next, 1);
-        cload(c, min(i + 5, last));
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (k % 2 == 0 && k < 14) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if (k == 14) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            if (k == 9) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-            if (k == 11 || k == 13) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        // the piece of B(s + 3): period (s + 3) / 2, issued at stage 2P - 4 (P >= 2) or in the
+        // prologue before A(1) and A(2) (P = 1)
+        if (steady || s + 3 < NS) {
+            if (steady) {
+                if (s & 1) vm_wait<AI>();
+                else vm_wait<2 * AI + CV>();
+            } else {
+                const int P = (s + 3) / 2;
+                int after = P == 1 ? after_p1 : 0;
+                for (int t = P == 1 ? 0 : 2 * P - 3; t <= s; ++t) after += ops_at(t);
+                vm_wait_n(after);
+            }
+            tie(nxt);
+            pc = pick(nxt, (s + 1) & 1);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
+        buf = nbuf;
     };
-    int i = 0;
-    for (; i + 3 <= nk; i += 3) {
-        iter(i + 0, 0, 1, 2, A0, A2, C2, C0);
-        iter(i + 1, 1, 2, 0, A1, A0, C0, C1);
-        iter(i + 2, 2, 0, 1, A2, A1, C1, C2);
+    using Dyn = std::integral_constant<bool, false>;
+    using Std = std::integral_constant<bool, true>;
+    // period P lives in code slot P % 2 (C0 / C1): stage s picks from period (s + 3) / 2 and
+    // even stages load period (s + 4) / 2
+    auto quad = [&](int s, auto steady_c) __attribute__((always_inline)) {
+        stage(s + 0, C1, C0, steady_c);
+        stage(s + 1, C0, C0, steady_c);
+        stage(s + 2, C0, C1, steady_c);
+        stage(s + 3, C1, C1, steady_c);
+    };
+    int s = 0;
+    if (NS >= 4) {
+        quad(0, Dyn{});
+        s = 4;
     }
-    if (i < nk) iter(i + 0, 0, 1, 2, A0, A2, C2, C0);
-    if (i + 1 < nk) iter(i + 1, 1, 2, 0, A1, A0, C0, C1);
+    for (; s + 8 <= NS; s += 4) quad(s, Std{});
+    for (; s + 4 <= NS; s += 4) quad(s, Dyn{});
+    if (s < NS) {
+        stage(s + 0, C1, C0, Dyn{});
+        stage(s + 1, C0, C0, Dyn{});
+    }
 
-    // ---- epilogue: accumulator (mt, nb) register r of lane l holds column
-    // 16*nb + 4*(l/16) + r of row 32*wave + 16*mt + l%16
-    const bool vec = m0 + BM <= M && n0 + BN <= N && (N & 3) == 0;
-    // (each wave uses only its own part of the buffers, which every wave finished reading
-    // at the loop's last barrier, so the exchanges are ordered within the wave)
-    // bf16 and SwiGLU outputs of a whole tile (rows 16-byte aligned): each wave passes its
-    // 16-row halves through LDS (the weight buffers, free after the last barrier; rows
-    // padded by 16 bytes, so the narrow writes of 16 rows and the 16-byte reads along a row
-    // are conflict-free) and stores whole rows (4 x 256 or 8 x 128 bytes per instruction)
-    // instead of 32- or 16-byte pieces of 16 rows, as non-temporal stores (the output is
-    // not read again by this kernel).  Each measured ~2 us faster on the prefill product.
-    if (OUT == 3 && vec && (N & 15) == 0) {
-        constexpr int OPITCH = 144;   // 64 bf16 outputs per row + 16
-        uint8_t* ob = reinterpret_cast<uint8_t*>(&Bs[0][0]) + wave * (16 * OPITCH);
+    // ---- epilogue.  Every wave is past the loop's last barrier (no LDS reads remain) and
+    // every load of the loop has completed.
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+        const int i = tid + GM_THREADS * e;
+        if (i < BM) xs_t[i] = ev[e];
+        else if (i < BM + BN) ws_t[i - BM] = ev[e];
+        else if (i < BM + 2 * BN) bias_t[i - BM - BN] = ev[e];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // accumulator (mt, nb) register r of lane l holds column wn*TN + 16nb + 4(l/16) + r of row
+    // wm*TM + 16mt + l%16
+    const bool whole = m0 + BM <= M && n0 + BN <= N;
+    // bf16 and SwiGLU outputs of a whole tile: each wave passes its 64 x 64 result through its
+    // own part of LDS (rows padded by 16 bytes, conflict-free) and stores whole row segments
+    // (8 rows x 128 bytes or 16 rows x 64 bytes per instruction) as non-temporal stores
+    if ((OUT == 0 || OUT == 3) && whole && (N & 15) == 0) {
+        constexpr int OW = OUT == 3 ? TN : 2 * TN;          // output bytes per row of the wave
+        constexpr int PITCH = OW + 16;
+        uint8_t* ob = reinterpret_cast<uint8_t*>(As) + wave * (TM * PITCH);
         const int rl = lane & 15, cq = lane >> 4;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const float xsm = xs_t[32 * wave + 16 * mt + rl];
+        for (int mt = 0; mt < MT; ++mt) {
+            const float xsm = xs_t[wm * TM + 16 * mt + rl];
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
+            for (int nb = 0; nb < NB; ++nb) {
                 const int nl = 16 * nb + 4 * cq;
-                const float4 wv = *reinterpret_cast<const float4*>(&ws_t[nl]);
-                const float4 bv = *reinterpret_cast<const float4*>(&bias_t[nl]);
+                const float4 wv = *reinterpret_cast<const float4*>(&ws_t[wn * TN + nl]);
+                const float4 bv = *reinterpret_cast<const float4*>(&bias_t[wn * TN + nl]);
                 const v4i a = acc[mt][nb];
                 const float wsv[4] = {wv.x, wv.y, wv.z, wv.w}, bsv[4] = {bv.x, bv.y, bv.z, bv.w};
                 float y[4];
@@ -286,72 +428,46 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
                     y[r] = __fmul_rn((float)a[r], __fmul_rn(xsm, wsv[r]));
                     if (bias) y[r] = __fadd_rn(y[r], bsv[r]);
                 }
-                // gate/up pairs (nl, nl + 1), (nl + 2, nl + 3) -> output columns nl/2, nl/2 + 1
-                *reinterpret_cast<uint32_t*>(ob + rl * OPITCH + nl) =
-                    f32x2_to_bf16x2(swiglu_f32(y[0], y[1]), swiglu_f32(y[2], y[3]));
-            }
-            wave_lds_sync();
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int row = (lane >> 3) + 8 * i, c = lane & 7;
-                const uint4 v = *reinterpret_cast<const uint4*>(ob + row * OPITCH + 16 * c);
-                const int64_t m = m0 + 32 * wave + 16 * mt + row;
-                __builtin_nontemporal_store(
-                    v4u{v.x, v.y, v.z, v.w},
-                    reinterpret_cast<v4u*>(reinterpret_cast<uint16_t*>(out) + m * (N >> 1) + (n0 >> 1) + 8 * c));
-            }
-            wave_lds_sync();
-        }
-        return;
-    }
-    if (OUT == 0 && vec && (N & 7) == 0) {
-        constexpr int OPITCH = 272;   // 128 bf16 outputs per row + 16
-        uint8_t* ob = reinterpret_cast<uint8_t*>(&Bs[0][0]) + wave * (16 * OPITCH);
-        const int rl = lane & 15, cq = lane >> 4;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const float xsm = xs_t[32 * wave + 16 * mt + rl];
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-                const int nl = 16 * nb + 4 * cq;
-                const float4 wv = *reinterpret_cast<const float4*>(&ws_t[nl]);
-                const float4 bv = *reinterpret_cast<const float4*>(&bias_t[nl]);
-                const v4i a = acc[mt][nb];
-                const float wsv[4] = {wv.x, wv.y, wv.z, wv.w}, bsv[4] = {bv.x, bv.y, bv.z, bv.w};
-                float y[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    y[r] = __fmul_rn((float)a[r], __fmul_rn(xsm, wsv[r]));
-                    if (bias) y[r] = __fadd_rn(y[r], bsv[r]);
+                uint8_t* dst = ob + (16 * mt + rl) * PITCH;
+                if (OUT == 3) {
+                    // gate/up pairs (nl, nl + 1), (nl + 2, nl + 3) -> output columns nl/2, nl/2 + 1
+                    *reinterpret_cast<uint32_t*>(dst + nl) =
+                        f32x2_to_bf16x2(swiglu_f32(y[0], y[1]), swiglu_f32(y[2], y[3]));
+                } else {
+                    *reinterpret_cast<uint2*>(dst + 2 * nl) =
+                        uint2{f32x2_to_bf16x2(y[0], y[1]), f32x2_to_bf16x2(y[2], y[3])};
                 }
-                *reinterpret_cast<uint2*>(ob + rl * OPITCH + 2 * nl) =
-                    uint2{f32x2_to_bf16x2(y[0], y[1]), f32x2_to_bf16x2(y[2], y[3])};
             }
-            wave_lds_sync();
+        }
+        wave_lds_sync();
+        constexpr int CPR = OW / 16, RPI = 64 / CPR;   // 16-byte chunks per row, rows per store
+        const int64_t row_elems = OUT == 3 ? (N >> 1) : N;
+        const int64_t col0 = OUT == 3 ? (n0 + wn * TN) >> 1 : n0 + wn * TN;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = cq + 4 * i;
-                const uint4 v = *reinterpret_cast<const uint4*>(ob + row * OPITCH + 16 * rl);
-                const int64_t m = m0 + 32 * wave + 16 * mt + row;
-                __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w},
-                                            reinterpret_cast<v4u*>(reinterpret_cast<uint16_t*>(out) + m * N + n0 + 8 * rl));
-            }
-            wave_lds_sync();
+        for (int i = 0; i < TM / RPI; ++i) {
+            const int row = RPI * i + lane / CPR, c = lane % CPR;
+            const uint4 v = *reinterpret_cast<const uint4*>(ob + row * PITCH + 16 * c);
+            const int64_t m = m0 + wm * TM + row;
+            __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w},
+                                        reinterpret_cast<v4u*>(reinterpret_cast<uint16_t*>(out) + m * row_elems +
+                                                               col0 + 8 * c));
         }
         return;
     }
+    const bool vec = whole && (N & 3) == 0;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        const int ml = 32 * wave + 16 * mt + (lane & 15), m = m0 + ml;
+    for (int mt = 0; mt < MT; ++mt) {
+        const int ml = wm * TM + 16 * mt + (lane & 15), m = m0 + ml;
+        if (m >= M) continue;
         const float xsm = xs_t[ml];
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-            const int nl = 16 * nb + 4 * (lane >> 4), n = n0 + nl;
+        for (int nb = 0; nb < NB; ++nb) {
+            const int nl = wn * TN + 16 * nb + 4 * (lane >> 4), n = n0 + nl;
             const float4 wv = *reinterpret_cast<const float4*>(&ws_t[nl]);
             const float4 bv = *reinterpret_cast<const float4*>(&bias_t[nl]);
             const v4i a = acc[mt][nb];
-            float y[4];
             const float wsv[4] = {wv.x, wv.y, wv.z, wv.w}, bsv[4] = {bv.x, bv.y, bv.z, bv.w};
+            float y[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 y[r] = __fmul_rn((float)a[r], __fmul_rn(xsm, wsv[r]));
@@ -364,22 +480,20 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
                 const uint32_t s01 = f32x2_to_bf16x2(swiglu_f32(y[0], y[1]), swiglu_f32(y[2], y[3]));
                 if (vec) {
                     *reinterpret_cast<uint32_t*>(o) = s01;
-                } else if (m < M) {
+                } else {
                     if (n + 1 < N) o[0] = (uint16_t)s01;
                     if (n + 3 < N) o[1] = (uint16_t)(s01 >> 16);
                 }
             } else if (vec) {
                 if (OUT == 0) {
-                    uint2 p;
-                    p.x = f32x2_to_bf16x2(y[0], y[1]);
-                    p.y = f32x2_to_bf16x2(y[2], y[3]);
-                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + idx) = p;
+                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + idx) =
+                        uint2{f32x2_to_bf16x2(y[0], y[1]), f32x2_to_bf16x2(y[2], y[3])};
                 } else if (OUT == 1) {
                     *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + idx) = float4{y[0], y[1], y[2], y[3]};
                 } else {
                     *reinterpret_cast<v4i*>(reinterpret_cast<int32_t*>(out) + idx) = a;
                 }
-            } else if (m < M) {
+            } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (n + r < N) store_out(out, OUT, idx + r, a[r], y[r]);
