@@ -52,6 +52,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-gemv", action="store_true")
     p.add_argument("--no-training", action="store_true", help="skip the training-path and variant kernels")
+    p.add_argument("--no-prefill-shapes", action="store_true", help="skip the M=4096 MLP pair and the M=8192 set")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device-to-device copy 5 times (counter calibration)")
     args = p.parse_args()
@@ -142,9 +143,11 @@ def bench_prefill(args, torch, B, device):
     # rotate_quant_act alone, after the timed region (an event before it in every step would
     # add a gap to the step)
     rq_ms, _ = timed_launches(torch, [rq_call], 20, int(args.sleep_cycles))
+    # the GEMM alone: median of 5 trials of 100 back-to-back launches (one event pair each)
+    gemm_med_ms = median_trials(torch, [gemm_call], 100, 5, int(args.sleep_cycles))
     ops = 2.0 * M * N * K
-    return dict(M=M, N=N, K=K, wall_s=wall, rq_ms=rq_ms, gemm_ms=gemm_ms, ops=ops, x_np=x_np, host=host,
-                quant_ms=quant_ms,
+    return dict(M=M, N=N, K=K, wall_s=wall, rq_ms=rq_ms, gemm_ms=gemm_ms, gemm_med_ms=gemm_med_ms, ops=ops,
+                x_np=x_np, host=host, quant_ms=quant_ms,
                 rq_bytes=3 * M * K + 4 * M,
                 gemm_bytes=weight_bytes(N, K) + M * K + 4 * M + 2 * M * N)
 
@@ -166,6 +169,70 @@ def timed_launches(torch, calls, n, sleep_cycles):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n, enqueue_s
+
+
+def median_trials(torch, calls, n, trials, sleep_cycles):
+    """Median over `trials` of the mean ms per launch of n back-to-back launches."""
+    return float(np.median([timed_launches(torch, calls, n, sleep_cycles)[0] for _ in range(trials)]))
+
+
+def launch_floor(args, torch, B):
+    """A kernel that does nothing, launched back to back like the GEMV sweep: the floor
+    any kernel of that grid pays for launch and drain (512 blocks of 256 threads is the
+    grid of the N = K = 4096 decode GEMV)."""
+    res = {}
+    for blocks in (512, 1024):
+        call = [lambda b=blocks: B.empty_launch(b, 256)]
+        ms = median_trials(torch, call, args.gemv_launches, 3, int(args.sleep_cycles))
+        res[f"{blocks}x256_us"] = round(ms * 1e3, 3)
+    return res
+
+
+def bench_prefill_shapes(args, torch, B, device, decode_layers=None):
+    """The MLP pair at M = 4096 (up 4096 x 12288 x 3072, down 4096 x 3072 x 12288; bf16
+    Student-t activations, nu = 4) and the 64-layer set at M = 8192 (the decode set's
+    layers; bf16 N(0, 1) activations drawn on the GPU), each GEMM timed as the median of
+    5 trials of back-to-back launches, rotate_quant_act separately."""
+    from bit_codebook_quantized_amd import synth
+    sleep = int(args.sleep_cycles)
+    res = {}
+    for name, (M, N, K, li) in {"mlp_up": (4096, 12288, 3072, 0), "mlp_down": (4096, 3072, 12288, 1)}.items():
+        w = synth.gaussian_weight_device(N, K, seed=synth.seed_for(3, li, synth.ROLE_WEIGHT), device=device)
+        layer = B.quantize_w4(w)
+        del w
+        x = torch.from_numpy(synth.activations(M, K, seed=synth.seed_for(3, li, synth.ROLE_ACT), kind="student_t")).to(
+            torch.bfloat16).to(device)
+        xq = torch.empty(M, K, dtype=torch.int8, device=device)
+        xs = torch.empty(M, dtype=torch.float32, device=device)
+        out = torch.empty(M, N, dtype=torch.bfloat16, device=device)
+        rq = B.prepared_rotate_quant(x, xq, xs)
+        gm = B.prepared_linear("w4a8_gemm", xq, xs, layer, out)
+        rq_ms = median_trials(torch, [rq], 50, 5, sleep)
+        g_ms = median_trials(torch, [gm], 100, 5, sleep)
+        ops = 2.0 * M * N * K
+        res[name] = {"M": M, "N": N, "K": K, "gemm_us": round(g_ms * 1e3, 2),
+                     "gemm_TOPS": round(ops / (g_ms * 1e-3) / 1e12, 1),
+                     "frac_int8_peak": round(ops / (g_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                     "rotate_quant_act_us": round(rq_ms * 1e3, 2),
+                     "layer_TOPS": round(ops / ((g_ms + rq_ms) * 1e-3) / 1e12, 1)}
+        del layer, x, xq, xs, out, rq, gm
+    if decode_layers:
+        M = 8192
+        xqs = {}
+        for k in sorted({l.in_features for l in decode_layers}):
+            x = synth.activations_device(M, k, seed=synth.seed_for(4, 100 + k // 3072, synth.ROLE_ACT), device=device)
+            xqs[k] = B.rotate_quant_act(x)
+            del x
+        outs = {n: torch.empty(M, n, dtype=torch.bfloat16, device=device)
+                for n in sorted({l.out_features for l in decode_layers})}
+        calls = [B.prepared_linear("w4a8_gemm", *xqs[l.in_features], l, outs[l.out_features]) for l in decode_layers]
+        ops = sum(2.0 * M * l.out_features * l.in_features for l in decode_layers)
+        set_ms = median_trials(torch, calls, len(calls), 5, sleep) * len(calls)
+        res["layer_set_M8192"] = {"layers": len(calls), "M": M, "set_us": round(set_ms * 1e3, 1),
+                                  "TOPS": round(ops / (set_ms * 1e-3) / 1e12, 1),
+                                  "frac_int8_peak": round(ops / (set_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
+        del calls, outs, xqs
+    return res
 
 
 def bench_gemv(args, torch, B, device):
@@ -250,7 +317,7 @@ def bench_decode_set(args, torch, B, device):
     timed_set([grouped], 2)
     seq_ms = timed_set(single, 10)
     grp_ms = timed_set([grouped], 10)
-    return {"layers": 64, "M": 1, "weight_bytes": wbytes,
+    return [it[2] for it in items], {"layers": 64, "M": 1, "weight_bytes": wbytes,
             "per_layer_launches_us": round(seq_ms * 1e3, 1),
             "per_layer_weight_GBps": round(wbytes / (seq_ms * 1e-3) / 1e9, 1),
             "grouped_us": round(grp_ms * 1e3, 1),
@@ -330,31 +397,55 @@ def bench_training(args, torch, B, device):
 
 
 def cpu_baseline(pre, min_seconds=10.0):
-    """The oracle, untuned, on the host cores: the whole M=2048 layer step (rotate +
-    quantise, decode, exact contraction, epilogue), repeated until at least
-    ``min_seconds`` of CPU work have been timed (bounded at 200 repetitions)."""
+    """The oracle, untuned, on the host cores: the M=2048 layer step split into its four
+    steps (rotate + quantise, int8-grid decode, exact fp64-BLAS contraction, epilogue),
+    each repeated until it has run for a share of ``min_seconds``; whole-step TOPS from
+    the sum of the four per-call times."""
     import oracle as O
     x = pre["x_np"]
     packed, srel, sch, cb = pre["host"]
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        xq, xs = O.rotate_quant_act(x)
-        w8 = O.decode_w4(packed, srel, cb)
-        acc = O.gemm_exact(xq, w8)
-        O.epilogue(acc, xs, sch, out="bf16")
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds or reps >= 200:
-            break
-    ops = 2.0 * pre["M"] * pre["N"] * pre["K"] * reps
+    M, N, K = pre["M"], pre["N"], pre["K"]
+    xq, xs = O.rotate_quant_act(x)
+    w8 = O.decode_w4(packed, srel, cb)
+    acc = O.gemm_exact(xq, w8)
+    steps = {"rotate_quant_act": lambda: O.rotate_quant_act(x),
+             "decode_w4": lambda: O.decode_w4(packed, srel, cb),
+             "gemm_exact_fp64_blas": lambda: O.gemm_exact(xq, w8),
+             "epilogue_bf16": lambda: O.epilogue(acc, xs, sch, out="bf16")}
+    share = {"rotate_quant_act": 0.2, "decode_w4": 0.15, "gemm_exact_fp64_blas": 0.5, "epilogue_bf16": 0.15}
+    per_call, detail = {}, {}
+    for name, fn in steps.items():
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds * share[name] or reps >= 200:
+                break
+        per_call[name] = dt / reps
+        detail[name] = {"s_per_call": round(dt / reps, 4), "reps": reps}
+    detail["rotate_quant_act"]["GBps"] = round((3 * M * K + 4 * M) / per_call["rotate_quant_act"] / 1e9, 2)
+    detail["decode_w4"]["GBps"] = round((N * K // 2 + N * K // 16 + N * K) / per_call["decode_w4"] / 1e9, 2)
+    detail["gemm_exact_fp64_blas"]["TOPS"] = round(2.0 * M * N * K / per_call["gemm_exact_fp64_blas"] / 1e12, 4)
+    detail["epilogue_bf16"]["GBps"] = round((8 * M * N + 4 * M + 4 * N + 2 * M * N) / per_call["epilogue_bf16"] / 1e9, 2)
+    total = sum(per_call.values())
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
-    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    return {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": min(cores, threads), "kind": "oracle",
-            "sample": f"the full M=2048 N=K=4096 step (rotate+quant, decode, exact fp64-BLAS contraction, "
-                      f"epilogue) x{reps}, {dt:.1f} s wall"}
+    blas, threads = "unknown", None
+    try:
+        from threadpoolctl import threadpool_info
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            blas = f"{infos[0].get('internal_api')} {infos[0].get('version')}"
+            threads = infos[0].get("num_threads")
+    except Exception:
+        pass
+    return {"value": round(2.0 * M * N * K / total / 1e12, 5), "unit": "TOPS",
+            "cores": threads if threads else cores, "kind": "oracle",
+            "sample": f"the M=2048 N=K=4096 step, its four steps timed separately ({total:.2f} s per step)",
+            "host_cores": cores, "blas": blas, "blas_threads": threads, "steps": detail}
 
 
 GEMM_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bit_codebook_quantized_amd", "csrc",
@@ -406,7 +497,10 @@ def main():
 
     pre = bench_prefill(args, torch, B, device)
     gemv = None if args.no_gemv else bench_gemv(args, torch, B, device)
-    decode_set = None if args.no_gemv else bench_decode_set(args, torch, B, device)
+    floor = None if args.no_gemv else launch_floor(args, torch, B)
+    decode_layers, decode_set = (None, None) if args.no_gemv else bench_decode_set(args, torch, B, device)
+    prefill_shapes = None if args.no_prefill_shapes else bench_prefill_shapes(args, torch, B, device, decode_layers)
+    del decode_layers
     training = None if args.no_training else bench_training(args, torch, B, device)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre)
 
@@ -430,8 +524,9 @@ def main():
                                "N(0,0.02^2) quantised by quantize_w4",
                    "M": pre["M"], "N": pre["N"], "K": pre["K"], "rot_block": 256, "group": 16},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": measured_traffic(),
-                     "kernel": "w4a8_gemm", "kernel_us": round(pre["gemm_ms"] * 1e3, 3)},
+                     "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": measured_traffic(),
+                     "kernel": "w4a8_gemm", "kernel_us": round(pre["gemm_ms"] * 1e3, 3),
+                     "kernel_us_median_5x100": round(pre["gemm_med_ms"] * 1e3, 3)},
         "quantize_w4": {"us": round(pre["quant_ms"] * 1e3, 1), "layer": "4096 x 4096 fp32, rotated on the fly",
                         "Mweights_per_s": round(pre["N"] * pre["K"] / (pre["quant_ms"] * 1e-3) / 1e6, 1),
                         "note": "offline weight quantisation, not part of the step"},
@@ -439,7 +534,9 @@ def main():
                              "GBps": round(pre["rq_bytes"] / (pre["rq_ms"] * 1e-3) / 1e9, 1),
                              "frac_hbm": round(pre["rq_bytes"] / (pre["rq_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "gemv": gemv,
+        "launch_floor": floor,
         "gemv_decode_set": decode_set,
+        "prefill_shapes": prefill_shapes,
         "training_and_variants": training,
         "cpu_baseline": cpu,
     }

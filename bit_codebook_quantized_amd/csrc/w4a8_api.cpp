@@ -37,6 +37,7 @@ hipError_t launch_lora_merge(const uint8_t* qpacked, const uint8_t* srel, const 
 hipError_t launch_dequantize(const uint8_t* qpacked, const uint8_t* srel, const float* codebook,
                              const float* s_channel, int64_t N, int K, int rotate_back, float* out,
                              hipStream_t stream);
+hipError_t launch_empty(int blocks, int threads, hipStream_t stream);
 hipError_t launch_quantize(const float* w, int64_t N, int K, int rotated, const float* codebook, uint8_t* qpacked,
                            uint8_t* srel, float* s_channel, hipStream_t stream);
 }  // namespace w4a8
@@ -303,6 +304,12 @@ const char* w4a8_status_string(int status) {
     }
 }
 
-int w4a8_abi_version(void) { return 8; }
+int w4a8_empty_launch(int32_t blocks, int32_t threads, void* stream) {
+    if (blocks < 1 || blocks > (1 << 20) || threads < 64 || threads > 1024 || threads % 64 != 0)
+        return W4A8_ERR_INVALID_ARG;
+    return launched(w4a8::launch_empty(blocks, threads, static_cast<hipStream_t>(stream)));
+}
+
+int w4a8_abi_version(void) { return 9; }
 
 }  // extern "C"

@@ -47,6 +47,16 @@ def gaussian_weight_device(n: int, k: int, seed: int, device, std: float = 0.02)
     return torch.randn(n, k, generator=g, device=device, dtype=torch.float32) * std
 
 
+def activations_device(m: int, k: int, seed: int, device):
+    """bf16 torch tensor [m, k] of N(0, 1) draws made on ``device`` by torch's generator
+    seeded with ``seed`` (for large benchmark activations; a different stream from
+    ``activations``)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(m, k, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
 def activations(m: int, k: int, seed: int, kind: str = "normal", nu: float = 4.0,
                 outlier_frac: float = 0.01, outlier_scale: float = 20.0,
                 outlier_seed: int | None = None) -> np.ndarray:

@@ -26,7 +26,7 @@ OUT_BF16, OUT_F32, OUT_I32, OUT_SWIGLU = 0, 1, 2, 3
 # gate/up-interleaved rows
 SWIGLU = "swiglu"
 ROT_BLOCK, GROUP, GEMV_MAX_M, MAX_K = 256, 16, 8, 131072
-ABI_VERSION = 8
+ABI_VERSION = 9
 FUSED_ACT_MAX_K = 4096   # linear() uses w4a8_gemv_act for one row up to this K
 _OUT_CODES = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32, torch.int32: OUT_I32, SWIGLU: OUT_SWIGLU}
 
@@ -66,6 +66,7 @@ SIGNATURES = {
     "lora_merge_w4": [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _I32, ctypes.c_float, _P, _P],
     "w4a8_status_string": [ctypes.c_int],
     "w4a8_abi_version": [],
+    "w4a8_empty_launch": [_I32, _I32, _P],
 }
 
 _lib = None
@@ -309,9 +310,12 @@ def w4a8_gemv_grouped(items, out_dtype=torch.bfloat16):
 
 
 def prepared_gemv_grouped(items, out_dtype=torch.bfloat16):
-    """prepare() for w4a8_gemv_grouped: the descriptor array is built and checked once."""
-    w4a8_gemv_grouped(items, out_dtype)                      # validates and runs once
-    arr, _, m = _group_descs(items, out_dtype)
+    """prepare() for w4a8_gemv_grouped: the descriptor array is built and checked once
+    (outputs given as None are allocated here, once).  The callable runs the group and
+    returns the outputs; it keeps every tensor it points at alive."""
+    if not items:
+        raise ValueError("prepared_gemv_grouped needs at least one layer")
+    arr, outs, m = _group_descs(items, out_dtype)
     c, dev, n = load().w4a8_gemv_grouped, items[0][0].device, len(items)
     code = _OUT_CODES[out_dtype]
 
@@ -319,7 +323,11 @@ def prepared_gemv_grouped(items, out_dtype=torch.bfloat16):
         st = c(ctypes.addressof(arr), n, m, GROUP, code, torch.cuda.current_stream(dev).cuda_stream)
         if st:
             _check("w4a8_gemv_grouped", st)
-    run.descs = arr   # keeps the array alive with the callable
+        return outs
+    run.descs = arr                      # the descriptor array
+    run.keep = (list(items), outs)       # the tensors behind its pointers
+    run.outs = outs
+    run()
     return run
 
 
@@ -464,6 +472,7 @@ def prepare(fn: str, *tensors_and_args):
         st = c(*args, torch.cuda.current_stream(dev).cuda_stream)
         if st:
             _check(fn, st)
+    run.keep = tuple(a for a in tensors_and_args if isinstance(a, torch.Tensor))   # the pointers' owners
     return run
 
 
@@ -486,6 +495,12 @@ def prepared_gemv_act(x, layer: W4A8Layer, out, qmax: int = 127, out_dtype=None)
     return prepare("w4a8_gemv_act", x, x.shape[0], ROT_BLOCK, qmax, layer.qpacked, layer.srel, layer.codebook,
                    layer.s_channel, bias, layer.out_features, layer.in_features, GROUP, _OUT_CODES[out_dtype], out,
                    None, None)
+
+
+def empty_launch(blocks: int, threads: int = 256, device="cuda") -> None:
+    """Launch the library's kernel that does nothing (a launch-floor measurement aid)."""
+    _check("w4a8_empty_launch", load().w4a8_empty_launch(int(blocks), int(threads),
+                                                         torch.cuda.current_stream(device).cuda_stream))
 
 
 def prepared_rotate_quant(x, xq, xs, qmax: int = 127):

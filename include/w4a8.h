@@ -337,6 +337,16 @@ int lora_merge_w4(const uint8_t* qpacked, const uint8_t* srel, const float* code
                   int64_t N, int64_t K, int32_t rot_block, int32_t group, const float* lora_a, const float* lora_b,
                   int32_t rank, float scale, float* out, void* stream);
 
+/*
+ * w4a8_empty_launch -- measurement aid, not a step of the layer: launches a kernel that
+ * does nothing, with `blocks` workgroups of `threads` threads, on `stream`.  Timing it
+ * back to back gives the launch-and-drain floor that any kernel of that grid pays, to
+ * set beside the decode GEMV's duration.
+ *   blocks    1 .. 2^20;  threads  64 .. 1024, a multiple of 64
+ * Errors: W4A8_ERR_INVALID_ARG outside those ranges; W4A8_ERR_HIP on a launch failure.
+ */
+int w4a8_empty_launch(int32_t blocks, int32_t threads, void* stream);
+
 /* Name of a status code ("W4A8_OK", ...); never NULL. */
 const char* w4a8_status_string(int status);
 

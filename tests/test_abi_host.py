@@ -29,9 +29,10 @@ def test_header_declares_the_operations():
     names = _declared_functions()
     for n in ("rotate_quant_act", "decode_w4_to_int8", "w4a8_gemm", "w4a8_gemv", "w4a8_gemv_grouped",
               "quantize_w4", "w4a8_gemv_act", "w4a8_gemv_act_max_k", "requantize_codes_w4", "fake_quant_w4",
-              "dequantize_w4", "w4a8_grad_input", "lora_merge_w4", "w4a8_status_string", "w4a8_abi_version"):
+              "dequantize_w4", "w4a8_grad_input", "lora_merge_w4", "w4a8_status_string", "w4a8_abi_version",
+              "w4a8_empty_launch"):
         assert n in names
-    assert len(names) == 15, names
+    assert len(names) == 16, names
 
 
 def test_library_exports_every_declared_symbol(w4a8):
@@ -46,7 +47,13 @@ def test_status_strings(w4a8):
         "W4A8_OK", "W4A8_ERR_INVALID_ARG", "W4A8_ERR_SHAPE", "W4A8_ERR_ALIGN", "W4A8_ERR_UNSUPPORTED",
         "W4A8_ERR_HIP"]
     assert w4a8.status_string(99) == "W4A8_ERR_UNKNOWN"
-    assert w4a8.load().w4a8_abi_version() == w4a8.ABI_VERSION == 8
+    assert w4a8.load().w4a8_abi_version() == w4a8.ABI_VERSION == 9
+
+
+def test_empty_launch_rejects_bad_grids(w4a8):
+    # validation happens before any HIP call, so this runs without a GPU
+    for blocks, threads in [(0, 256), (-1, 64), ((1 << 20) + 1, 64), (4, 32), (4, 100), (4, 2048)]:
+        assert w4a8.call("w4a8_empty_launch", blocks, threads, None) == w4a8.ERR_INVALID_ARG
 
 
 A = 1 << 20          # a 16-byte-aligned fake address (never dereferenced: validation fails first)

@@ -88,3 +88,27 @@ def test_grouped_prepared_call_and_empty():
     ref = B.w4a8_gemv(xq, xs, layer)
     assert np.array_equal(as_bits(out), as_bits(ref))
     assert B.w4a8_gemv_grouped([]) == []
+
+
+def test_grouped_prepared_call_allocates_missing_outputs_once():
+    # outputs given as None are allocated by prepared_gemv_grouped and kept with the
+    # callable, which writes them on every call and returns them
+    items = []
+    for i, (n, k) in enumerate([(300, 512), (1000, 3072), (37, 256)]):
+        layer = layer_from_bytes(n, k, seed=40 + i, with_bias=i == 1)
+        xq, xs = acts(3, k, 50 + i)
+        items.append((xq, xs, layer, None))
+    say("prepared grouped gemv with outputs allocated by the binding")
+    run = B.prepared_gemv_grouped(items)
+    outs = run()
+    assert outs is run.outs and len(outs) == 3
+    ptrs = [o.data_ptr() for o in outs]
+    for o in outs:
+        o.zero_()
+    torch.cuda.synchronize()
+    # other allocations in between must not take over the bound outputs
+    scratch = [torch.full((3, 4096), 7, dtype=torch.bfloat16, device=DEV) for _ in range(8)]
+    assert run() is outs and [o.data_ptr() for o in outs] == ptrs
+    for (xq, xs, layer, _), o in zip(items, outs):
+        assert np.array_equal(as_bits(o), as_bits(B.w4a8_gemv(xq, xs, layer)))
+    del scratch
