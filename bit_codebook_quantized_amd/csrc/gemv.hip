@@ -198,6 +198,7 @@ __device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds,
     const float qmaxf = (float)qmax;
     float r[16];
     float amax = 0.0f, scale = 1.0f;
+    bool poisoned = false;
     double inv = 1.0;
 
     auto load_job = [&](int j) __attribute__((always_inline)) {
@@ -212,8 +213,7 @@ __device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds,
         rotate_loaded<true>(in, ok, slot, l16, tbuf, r);   // exchanges within each slot's wave
         if (pass1) {
             if (cc == 0) amax = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(r[i]));
+            amax = block_absmax(r, amax);
             if (cc == nch - 1) {
                 const float a = slot_max(amax);
                 // alternate rows: every thread reads row r's maxima before it reaches row r + 1's
@@ -224,8 +224,9 @@ __device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds,
                 float rmax = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) rmax = __builtin_fmaxf(rmax, sm[i]);
-                scale = rmax > 0.0f ? rmax / qmaxf : 1.0f;   // IEEE fp32 division
-                inv = 1.0 / (double)scale;
+                scale = row_scale(rmax, qmaxf);
+                poisoned = row_poisoned(rmax);   // block-uniform: the block holds one row
+                inv = poisoned ? 0.0 : 1.0 / (double)scale;
                 if (tid == 0) {
                     xs_lds[row] = scale;
                     if (xs_out) xs_out[row] = scale;
@@ -235,7 +236,8 @@ __device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds,
         if ((nch == 1 || !pass1) && ok) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                act[row * SLAB + act_chunk(16 * blk + i) * 16 + act_byte(l16)] = quant1(r[i], inv, qmaxf);
+                act[row * SLAB + act_chunk(16 * blk + i) * 16 + act_byte(l16)] =
+                    poisoned ? (uint8_t)0 : quant1(r[i], inv, qmaxf);
         }
     };
 

@@ -8,10 +8,16 @@
 // out_i = (a0 + a1 + a2 + a3) - 2 a_(3-i); four stages, one per base-4 digit of
 // the column index, give the whole block.
 //
-// Precision: inputs are bf16 (8 significant bits).  The stages run in fp64, where
-// every partial sum of +-x terms is exact unless the block's exponent spread
-// exceeds ~37 binades, so the result equals the exact block product; it is rounded
-// once to fp32.  This is the value the quantiser sees.
+// Precision: inputs are bf16 (8 significant bits).  The stages run in fp64.  After
+// stage t a value is a sum of 4^t inputs halved t times: below 2^(E + 1 + t) in
+// magnitude (E the exponent of the block's largest input) and a multiple of 2^(L - t)
+// (L the exponent of the lowest set significand bit among its non-zero inputs), so
+// every partial sum is exact while E - L <= 44 (for bf16: every non-zero magnitude
+// within 2^37 of the block's largest).  The result is then the exact block product,
+// rounded once to fp32.  This is the value the quantiser sees.
+//
+// Non-finite values: a row any of whose rotated values is not finite (an inf or NaN
+// input, or a block whose product overflows fp32) gets scale NaN and all codes 0.
 //
 // Quantisation (ai-toolkit convrot_w4a8_quant.py, w4a8_act_quant_kernel): amax =
 // max |v| over the row, scale = amax / qmax in fp32 (1.0 when amax is 0),
@@ -75,8 +81,7 @@ __global__ __launch_bounds__(RQ_THREADS) void rotate_quant_kernel(const uint16_t
             if (c < nch) {
                 const int blk = blk0 + 16 * c;
                 rotate_block<true>(x, row, K, blk, row_ok && blk < nb, slot, l16, tbuf, keep[c]);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(keep[c][i]));
+                amax = block_absmax(keep[c], amax);
             }
         }
     } else {
@@ -84,8 +89,7 @@ __global__ __launch_bounds__(RQ_THREADS) void rotate_quant_kernel(const uint16_t
             const int blk = blk0 + 16 * c;
             float r[16];
             rotate_block<true>(x, row, K, blk, row_ok && blk < nb, slot, l16, tbuf, r);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(r[i]));
+            amax = block_absmax(r, amax);
         }
     }
 
@@ -99,8 +103,9 @@ __global__ __launch_bounds__(RQ_THREADS) void rotate_quant_kernel(const uint16_t
     } else {
         for (int s = 0; s < 16; ++s) rmax = __builtin_fmaxf(rmax, smax[s]);
     }
-    const float scale = rmax > 0.0f ? rmax / qmaxf : 1.0f;   // IEEE fp32 division
-    const double inv = 1.0 / (double)scale;
+    const float scale = row_scale(rmax, qmaxf);
+    const bool poisoned = row_poisoned(rmax);
+    const double inv = poisoned ? 0.0 : 1.0 / (double)scale;
     if (row_ok && l16 == 0 && blk0 == 0) xs[row] = scale;
 
     if (CH > 0) {
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(RQ_THREADS) void rotate_quant_kernel(const uint16_t
         for (int c = 0; c < KEEP; ++c) {
             if (c < nch) {
                 const int blk = blk0 + 16 * c;
-                quant_store(keep[c], inv, qmaxf, row_ok && blk < nb, xq, row, K, blk, l16, qb);
+                quant_store(keep[c], inv, qmaxf, row_ok && blk < nb, poisoned, xq, row, K, blk, l16, qb);
             }
         }
     } else {
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(RQ_THREADS) void rotate_quant_kernel(const uint16_t
             const int blk = blk0 + 16 * c;
             float r[16];
             rotate_block<true>(x, row, K, blk, row_ok && blk < nb, slot, l16, tbuf, r);
-            quant_store(r, inv, qmaxf, row_ok && blk < nb, xq, row, K, blk, l16, qb);
+            quant_store(r, inv, qmaxf, row_ok && blk < nb, poisoned, xq, row, K, blk, l16, qb);
         }
     }
 }

@@ -120,6 +120,25 @@ __device__ __forceinline__ float slot_max(float a) {
     return a;
 }
 
+// Running maximum |v| over a lane's rotated block r.  fmaxf drops a NaN, so a block with a
+// non-finite value is mapped to +inf through r[0]: a non-finite input makes every output of
+// its block non-finite, and an output that overflows fp32 is +-inf, which the maximum keeps.
+__device__ __forceinline__ float block_absmax(const float (&r)[16], float amax) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(r[i]));
+    return (r[0] - r[0] != 0.0f) ? __builtin_inff() : amax;   // r - r is NaN for inf and NaN
+}
+
+// A row is poisoned when its maximum is not finite: its scale is NaN and all its codes 0.
+__device__ __forceinline__ bool row_poisoned(float rmax) { return !(rmax <= 3.402823466e38f); }
+
+// The row scale: amax / qmax as an IEEE fp32 division, 1.0 for an all-zero row, NaN for a
+// poisoned row.
+__device__ __forceinline__ float row_scale(float rmax, float qmaxf) {
+    if (row_poisoned(rmax)) return __builtin_nanf("");
+    return rmax > 0.0f ? rmax / qmaxf : 1.0f;
+}
+
 __device__ __forceinline__ uint8_t quant1(float v, double inv, float qmaxf) {
     // Adding 1.5 * 2^23 rounds |x| < 2^22 to an integer half-to-even (the one fp32 add),
     // and the sum's low byte is then that integer mod 256.  The clamp is applied to the
@@ -134,13 +153,15 @@ __device__ __forceinline__ uint8_t quant1(float v, double inv, float qmaxf) {
 // Quantise one rotated block held as r[i] = column 16*i + l16 and store it: the slot's
 // 16 lanes transpose the codes through their own 256 bytes of LDS, qb (16-byte aligned;
 // the slot's lanes are in one wave, so the accesses are ordered within the wave only).
-__device__ __forceinline__ void quant_store(const float (&r)[16], double inv, float qmaxf, bool ok,
+// A poisoned row (one slot = one row) stores zeros.
+__device__ __forceinline__ void quant_store(const float (&r)[16], double inv, float qmaxf, bool ok, bool poisoned,
                                             int8_t* __restrict__ xq, int64_t row, int K, int blk,
                                             int l16, uint8_t* qb) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) qb[16 * i + l16] = quant1(r[i], inv, qmaxf);
     wave_lds_sync();
-    const uint4 out = *reinterpret_cast<const uint4*>(qb + 16 * l16);
+    uint4 out = *reinterpret_cast<const uint4*>(qb + 16 * l16);
+    if (poisoned) out = make_uint4(0u, 0u, 0u, 0u);
     if (ok) *reinterpret_cast<uint4*>(xq + row * K + (int64_t)blk * 256 + 16 * l16) = out;
     wave_lds_sync();
 }

@@ -86,8 +86,18 @@ enum w4a8_out_type {
  * Follows h3-rs weights.rs fn rotate_activation (block rotation of the last dim by the
  * Kronecker-power Hadamard of fn hadamard, divided by 16 for block 256) and ai-toolkit
  * w4a8_act_quant_kernel (per-row absmax, scale = amax / qmax or 1.0 for a zero row,
- * q = round_half_even(v / scale) clamped to [-qmax, qmax]).  The rotated value v is
- * the exact block product rounded once to fp32; the division is the IEEE fp32 one.
+ * q = round_half_even(v / scale) clamped to [-qmax, qmax]).  The division is the IEEE
+ * fp32 one.  The rotated value v is the exact block product rounded once to fp32
+ * whenever, in every 256-column block, E - L <= 44, with E the exponent of the largest
+ * input magnitude and L the exponent of the lowest set significand bit among the
+ * non-zero inputs (for bf16 this holds when every non-zero magnitude of a block lies
+ * within 2^37 of the block's largest); the fp64 stages are exact there.  Blocks beyond
+ * that bound get the fp64 stages' rounding (a few units of 2^-53 of the largest
+ * partial sum) before the one rounding to fp32.
+ * Non-finite values: a row any of whose rotated values is not finite (an inf or NaN
+ * input, or a block whose product overflows fp32) gets xs = NaN and all codes 0, so
+ * every output of that row in w4a8_gemm / w4a8_gemv is NaN.  w4a8_gemv_act applies
+ * the same rule.
  *
  *   x         in   bf16 bits [M, K]
  *   M, K           rows and columns

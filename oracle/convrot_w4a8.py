@@ -227,7 +227,8 @@ def rotate_to_f32(x, block: int = ROT_BLOCK) -> np.ndarray:
     if x.shape[-1] % block:
         raise ValueError(f"block {block} does not divide {x.shape}")
     blocks = x.reshape(-1, block)
-    out = (blocks.astype(np.float64) @ hadamard(block)).astype(F32)
+    with np.errstate(over="ignore", invalid="ignore"):    # overflow to inf is the IEEE rounding
+        out = (blocks.astype(np.float64) @ hadamard(block)).astype(F32)
     finite = np.isfinite(blocks).all(axis=1)
     out[~finite] = np.nan
     m, e = _f32_parts(np.where(np.isfinite(blocks), blocks, F32(0.0)))

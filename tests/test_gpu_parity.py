@@ -149,6 +149,80 @@ def test_rotate_quant_act_extreme_magnitudes():
         assert np.array_equal(xq.cpu().numpy(), rq)
 
 
+def _bf16_exact(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).float().numpy()
+
+
+@pytest.mark.parametrize("spread", [30, 37, 44])
+def test_rotate_quant_act_at_the_exactness_bound(spread):
+    # every 256-column block spans `spread` binades from the exponent of its largest input
+    # (E = 0) to the lowest set significand bit of its smallest (2^-spread); up to 44 every
+    # fp64 partial sum of the rotation is exact, so the result is the exact block product
+    # rounded once, as the oracle forms it with integers where fp64 would not be exact
+    rng = synth.rng(300 + spread)
+    m, k = 6, 1024
+    x = (rng.standard_normal((m, k)) * 0.25).astype(np.float32)
+    x[np.abs(x) < 2.0 ** -20] = 0.0
+    x = _bf16_exact(x)
+    x[:, 0::256] = 1.9921875
+    x[:, 1::256] = np.float32(2.0 ** -spread)
+    x[:, 2::256] = -np.float32(3.0 * 2.0 ** -spread)
+    x[3, 256:512] = 0.0
+    x[3, 300] = np.float32(2.0 ** -spread)          # a block holding only the smallest value
+    say("rotate_quant_act exactness bound, spread", spread)
+    xq, xs = B.rotate_quant_act(bf16_dev(x))
+    rq, rs = O.rotate_quant_act(x)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(xq.cpu().numpy(), rq)
+
+
+def _non_finite_rows(m, k, seed):
+    x = synth.activations(m, k, seed=seed)
+    h0 = np.sign(O.hadamard(256)[0]).astype(np.float32)
+    x[1, 5] = np.inf
+    x[2, k - 3] = -np.inf
+    x[3, 300 % k] = np.nan
+    x[4, :256] = h0 * np.float32(3.3895313892515355e38)   # the largest bf16: its block overflows fp32
+    x[5, 3] = np.inf
+    x[5, 9] = -np.inf
+    return x
+
+
+def test_rotate_quant_act_rows_with_non_finite_values():
+    # a row holding an inf or NaN input, or a block whose rotated value overflows fp32, has
+    # no finite maximum: scale NaN and every code 0 (the oracle's reading); other rows as usual
+    for m, k in [(8, 1024), (16, 256), (3, 8192), (7, 40960)]:
+        x = _non_finite_rows(max(m, 6), k, seed=91 + k)
+        say("rotate_quant_act non-finite rows", x.shape)
+        xq, xs = B.rotate_quant_act(bf16_dev(x))
+        rq, rs = O.rotate_quant_act(x)
+        assert np.array_equal(xs.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+        assert np.array_equal(xq.cpu().numpy(), rq)
+        assert np.all(np.isnan(rs[1:6])) and np.all(rq[1:6] == 0)
+
+
+def test_layer_outputs_of_non_finite_rows_are_nan():
+    # through the whole layer: the poisoned rows' outputs are NaN (0 * NaN scale), the other
+    # rows are bit-exact; GEMM (12 rows), GEMV and the one-launch GEMV (6 rows)
+    packed, srel, sch, cb = quantized_layer(384, 1024, config=9)
+    layer = host_layer(packed, srel, sch, cb)
+    for m in (12, 6):
+        x = _non_finite_rows(m, 1024, seed=97)
+        ref, *_ = O.linear(x, packed, srel, sch, cb, out="bf16")
+        say("layer with non-finite rows, M =", m)
+        y = bf16_bits(B.linear(bf16_dev(x), layer))
+        assert np.array_equal(y, ref)
+        if m <= 8:
+            xq_o = torch.empty(m, 1024, dtype=torch.int8, device=DEV)
+            xs_o = torch.empty(m, dtype=torch.float32, device=DEV)
+            y2 = bf16_bits(B.w4a8_gemv_act(bf16_dev(x), layer, xq_out=xq_o, xs_out=xs_o))
+            assert np.array_equal(y2, ref)
+            rq, rs = O.rotate_quant_act(x)
+            assert np.array_equal(xs_o.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+            assert np.array_equal(xq_o.cpu().numpy(), rq)
+        assert np.all(np.isnan(O.bf16_bits_to_f32(ref[1:6])))
+
+
 # ------------------------------------------------------------- integer contraction
 
 # (256, 256, 256) and (513, 384, 1024): whole 256 x 128 tiles (their bf16 output goes through
