@@ -10,13 +10,14 @@
 //
 // Layout.  A block of 256 threads = 4 waves; wave w owns R consecutive output rows.
 // Its 64 lanes split K into 16-column groups (8 bytes of codes + 1 scale byte).  A
-// batch covers 4096 columns: lane l takes the 4 consecutive groups 4l .. 4l + 3 of
-// each row (two 16-byte code loads and one scale dword per row, each instruction
-// reading contiguous memory).  A batch's weight loads for all R rows are issued
-// together and the next batch is prefetched while the current one is decoded.  The
-// first batch is issued before the block builds its 256 x 16 level table in LDS and
-// stages the int8 activations (M x up to 32 KiB, reused by all R rows of all 4
-// waves) in LDS.
+// batch covers 64 * NB groups: lane l takes the NB consecutive groups NB*l .. NB*l + NB - 1
+// of each row (NB = 4: two 16-byte code loads and one scale dword per row; NB = 3, for K
+// a multiple of 3072 and not of 4096: a 16-byte and an 8-byte code load and one 8-byte
+// scale load, so that no lane idles when K = 3072).  A batch's weight loads for all R rows
+// are issued together and the next batch is prefetched while the current one is decoded.
+// The first batch is issued before the block builds its 256 x 16 level table in LDS and
+// stages the int8 activations (M x up to 32 KiB, reused by all R rows of all 4 waves) in
+// LDS.
 //
 // Arithmetic per 16-column group and row: one LDS read of the 16-level table row
 // of the group's scale byte, two 8-code byte-permute decodes that return even
@@ -25,6 +26,7 @@
 // registers for the whole of K and are combined across the wave once, by a
 // reduce-scatter (each halving step exchanges half the values), so a lane ends
 // with one fully summed output.
+#include <atomic>
 #include <type_traits>
 
 #include "../../include/w4a8.h"
@@ -35,9 +37,8 @@ namespace w4a8 {
 namespace {
 
 constexpr int GV_THREADS = 256;
-constexpr int GV_BATCH = 4;   // groups per lane per batch
-constexpr int GEMV_GROUP_MAX = 32;   // layers per grouped launch (the table fits the kernel arguments)
-constexpr int64_t GV_GROUP_BLOCKS = 4096;   // blocks a grouped call is cut into (all its launches)
+constexpr int GEMV_GROUP_MAX = 64;   // layers per grouped launch (the table travels in the kernel arguments)
+constexpr int GV_ROUNDS = 4;         // a grouped launch is at most this many rounds of resident blocks
 
 constexpr int pow2_ceil(int v) { return v <= 1 ? 1 : 2 * pow2_ceil((v + 1) / 2); }
 constexpr int log2i(int v) { return v <= 1 ? 0 : 1 + log2i(v / 2); }
@@ -45,34 +46,66 @@ constexpr int log2i(int v) { return v <= 1 ? 0 : 1 + log2i(v / 2); }
 // Columns of activations held in LDS at a time.
 __host__ __device__ constexpr int slab_cols(int mm) { return mm == 1 ? 32768 : mm == 2 ? 16384 : mm <= 4 ? 8192 : 4096; }
 
-// A batch: lane l takes the 4 consecutive groups 4l .. 4l + 3 of the batch's 256 (64
-// columns) of each of its R rows: 32 bytes of codes (two 16-byte loads) and the 4 scale
-// bytes (one dword), three wide loads per row.
-template <int R>
+// A batch: lane l takes the NB consecutive groups NB*l .. NB*l + NB - 1 of the batch's
+// 64*NB of each of its R rows: 8*NB bytes of codes (q[r][2u], q[r][2u + 1] = group u)
+// and the NB scale bytes (byte u of s[r]).
+template <int R, int NB>
 struct Batch {
-    uint4 q[2][R];
+    uint32_t q[R][2 * NB];
     uint32_t s[R];
     float w[R], b[R];   // the rows' channel scales and biases (epilogue operands)
 };
 
-// Loads are unconditional (lanes past the row end re-read its last 4 groups), so the
+// 16 and 8 bytes at 8-byte (code rows) or 4-byte (scale rows) aligned addresses
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+
+// Groups per lane and batch for a K-column row whose activations fit one slab: 3 when
+// that leaves fewer lanes idle than 4 and K / 16 is a multiple of 3 (a lane's groups
+// are then all inside the row or all past it), else 4.
+__host__ __device__ constexpr int gemv_nb(int K, int slab) {
+    const int g = K >> 4;
+    const int idle4 = (g + 255) / 256 * 256 - g, idle3 = (g + 191) / 192 * 192 - g;
+    return (K <= slab && g % 3 == 0 && idle3 < idle4) ? 3 : 4;
+}
+
+// Loads are unconditional (lanes past the row end re-read its last groups), so the
 // compiler can count the loads in flight and wait for exactly the batch it needs.
-template <int R>
-__device__ __forceinline__ void load_batch(Batch<R>& b, const uint8_t* const (&qrow)[R], const uint8_t* const (&srow)[R],
+template <int R, int NB>
+__device__ __forceinline__ void load_batch(Batch<R, NB>& b, const uint8_t* const (&qrow)[R], const uint8_t* const (&srow)[R],
                                            int jbase, int nchunk) {
-    const int j = min(jbase, nchunk - 4);   // nchunk is a multiple of 16
+    const int j = min(jbase, nchunk - NB);   // nchunk is a multiple of 16 (and of 3 for NB = 3)
+    if constexpr (NB == 4) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        b.q[0][r] = *reinterpret_cast<const uint4*>(qrow[r] + (int64_t)j * 8);
-        b.q[1][r] = *reinterpret_cast<const uint4*>(qrow[r] + (int64_t)j * 8 + 16);
-        b.s[r] = *reinterpret_cast<const uint32_t*>(srow[r] + j);
+        for (int r = 0; r < R; ++r) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(qrow[r] + (int64_t)j * 8);
+            const uint4 hi = *reinterpret_cast<const uint4*>(qrow[r] + (int64_t)j * 8 + 16);
+            b.q[r][0] = lo.x; b.q[r][1] = lo.y; b.q[r][2] = lo.z; b.q[r][3] = lo.w;
+            b.q[r][4] = hi.x; b.q[r][5] = hi.y; b.q[r][6] = hi.z; b.q[r][7] = hi.w;
+            b.s[r] = *reinterpret_cast<const uint32_t*>(srow[r] + j);
+        }
+    } else {
+        // the 3 scale bytes j .. j + 2 from the 8 bytes at the dword below j, moved back to
+        // stay inside the row (nchunk - 8 <= j4 <= j, j - j4 <= 5)
+        const int j4 = min(j & ~3, nchunk - 8), sh = 8 * (j - j4);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const u32x4_a4 lo = *reinterpret_cast<const u32x4_a4*>(qrow[r] + (int64_t)j * 8);
+            const u32x2_a4 hi = *reinterpret_cast<const u32x2_a4*>(qrow[r] + (int64_t)j * 8 + 16);
+            b.q[r][0] = lo.x; b.q[r][1] = lo.y; b.q[r][2] = lo.z; b.q[r][3] = lo.w;
+            b.q[r][4] = hi.x; b.q[r][5] = hi.y;
+            const u32x2_a4 sv = *reinterpret_cast<const u32x2_a4*>(srow[r] + j4);
+            b.s[r] = (uint32_t)((((uint64_t)sv.y << 32) | sv.x) >> sh);
+        }
     }
 }
 
-// Position of 16-byte chunk c of an activation slab in LDS: the two low bits are XORed
-// with bits 4-5, so the 16 lanes of a read (chunks 4l + u, l = 0..15) hit 16 different
-// bank groups.
-__device__ __forceinline__ int act_chunk(int c) { return c ^ ((c >> 4) & 3); }
+// Position of 16-byte chunk c of an activation slab in LDS.  NB = 4: the two low bits
+// are XORed with bits 4-5, so the 16 lanes of a read (chunks 4l + u, l = 0..15) hit 16
+// different bank groups.  NB = 3: unchanged (chunks 3l + u of 16 consecutive lanes are
+// already 16 different ones modulo 16).
+template <int NB>
+__device__ __forceinline__ int act_chunk(int c) { return NB == 4 ? c ^ ((c >> 4) & 3) : c; }
 
 // Inside a chunk each 8-column half is stored even columns first: bytes k0 k2 k4 k6 k1 k3
 // k5 k7, the order in which decode_split returns the weights, so the products need no
@@ -93,8 +126,7 @@ __device__ __forceinline__ int act_byte(int j) { return (j & 8) | ((j & 1) << 2)
 // LDS where gfx950 has a register path: the permlane swaps for 32 and 16 (each returns
 // this lane's value and its partner's, in an order set by the lane's half or row
 // parity), DPP for 8 (row rotate) and for 2 and 1 (quad permutes); 4 takes a swizzle.
-__device__ __forceinline__ int32_t lane_xor(int32_t v, int o) {
-    const int lane = (int)(threadIdx.x & 63);
+__device__ __forceinline__ int32_t lane_xor(int32_t v, int o, int lane) {
     if (o == 32) {
         const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
         return (int32_t)(lane < 32 ? r[1] : r[0]);
@@ -115,15 +147,15 @@ __device__ __forceinline__ int32_t lane_xor(int32_t v, int o) {
 // there).  NC uint4 per thread and row, a compile-time count (an index guarded by a
 // run-time test would keep the staging registers in scratch memory): chunks past the row
 // end are clamped to its last chunk and rewrite it with the same bytes.
-template <int MM, int NC, typename F>
+template <int MM, int NB, int NC, typename F>
 __device__ __forceinline__ void stage_acts_n(uint8_t* act, const int8_t* __restrict__ xq, int K, int k0, int per_row,
-                                             F&& between) {
+                                             int tid, F&& between) {
     uint4 v[MM][NC];
 #pragma unroll
     for (int m = 0; m < MM; ++m)
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const int i = min((int)threadIdx.x + 256 * c, per_row - 1);
+            const int i = min(tid + 256 * c, per_row - 1);
             v[m][c] = *reinterpret_cast<const uint4*>(xq + (int64_t)m * K + k0 + i * 16);
         }
     between();
@@ -131,20 +163,20 @@ __device__ __forceinline__ void stage_acts_n(uint8_t* act, const int8_t* __restr
     for (int m = 0; m < MM; ++m)
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const int i = min((int)threadIdx.x + 256 * c, per_row - 1);
-            *reinterpret_cast<uint4*>(act + m * slab_cols(MM) + act_chunk(i) * 16) = act_split(v[m][c]);
+            const int i = min(tid + 256 * c, per_row - 1);
+            *reinterpret_cast<uint4*>(act + m * slab_cols(MM) + act_chunk<NB>(i) * 16) = act_split(v[m][c]);
         }
 }
 
-template <int MM, typename F>
+template <int MM, int NB, typename F>
 __device__ __forceinline__ void stage_acts(uint8_t* act, const int8_t* __restrict__ xq, int K, int k0, int cols,
-                                           F&& between) {
+                                           int tid, F&& between) {
     constexpr int PER = slab_cols(MM) / 16 / 256;   // at most 8
     const int per_row = cols >> 4;
-    if (per_row <= 256 || PER == 1) stage_acts_n<MM, 1>(act, xq, K, k0, per_row, between);
-    else if (per_row <= 512 || PER == 2) stage_acts_n<MM, (PER < 2 ? PER : 2)>(act, xq, K, k0, per_row, between);
-    else if (per_row <= 1024 || PER == 4) stage_acts_n<MM, (PER < 4 ? PER : 4)>(act, xq, K, k0, per_row, between);
-    else stage_acts_n<MM, PER>(act, xq, K, k0, per_row, between);
+    if (per_row <= 256 || PER == 1) stage_acts_n<MM, NB, 1>(act, xq, K, k0, per_row, tid, between);
+    else if (per_row <= 512 || PER == 2) stage_acts_n<MM, NB, (PER < 2 ? PER : 2)>(act, xq, K, k0, per_row, tid, between);
+    else if (per_row <= 1024 || PER == 4) stage_acts_n<MM, NB, (PER < 4 ? PER : 4)>(act, xq, K, k0, per_row, tid, between);
+    else stage_acts_n<MM, NB, PER>(act, xq, K, k0, per_row, tid, between);
 }
 
 // Bytes of dynamic LDS of a GEMV block: level table, activation slab, the rows' scales,
@@ -184,7 +216,7 @@ __device__ __forceinline__ RotIn rot_first_job(const uint16_t* __restrict__ x, i
     return rot_job_load(x, K, j, MM * jpr, jpr, nch);
 }
 
-template <int MM, bool LONGK>
+template <int MM, int NB, bool LONGK>
 __device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds, double* tbuf, float* smax,
                                                     const uint16_t* __restrict__ x, int K, int qmax,
                                                     const RotIn first0, const RotIn first1,
@@ -236,7 +268,7 @@ __device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds,
         if ((nch == 1 || !pass1) && ok) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                act[row * SLAB + act_chunk(16 * blk + i) * 16 + act_byte(l16)] =
+                act[row * SLAB + act_chunk<NB>(16 * blk + i) * 16 + act_byte(l16)] =
                     poisoned ? (uint8_t)0 : quant1(r[i], inv, qmaxf);
         }
     };
@@ -268,7 +300,7 @@ __device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds,
         for (int i = tid; i < MM * per_row; i += GV_THREADS) {
             const int m = i / per_row, c = i - m * per_row;
             *reinterpret_cast<uint4*>(xq_out + (int64_t)m * K + c * 16) =
-                act_merge(*reinterpret_cast<const uint4*>(act + m * SLAB + act_chunk(c) * 16));
+                act_merge(*reinterpret_cast<const uint4*>(act + m * SLAB + act_chunk<NB>(c) * 16));
         }
     }
 }
@@ -277,7 +309,7 @@ __device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds,
 // rotate_quant_to_lds; K <= slab_cols(MM)) instead of xq / xs.
 // CARRY: the tile's channel scales and biases are loaded with each batch (for blocks that
 // walk several tiles); otherwise they are loaded once, in the tile's epilogue.
-template <int MM, int R, bool FUSED = false, bool LONGK = false, bool CARRY = false>
+template <int MM, int R, int NB, bool FUSED = false, bool LONGK = false, bool CARRY = false>
 __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const float* __restrict__ xs,
                                           const uint8_t* __restrict__ qp, const uint8_t* __restrict__ srel,
                                           const float* __restrict__ codebook, const float* __restrict__ ws,
@@ -293,16 +325,30 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
     constexpr int WAVES = GV_THREADS / 64;
 
     // the wave index as a uniform value, so row-dependent scalars use scalar loads
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    // the thread index through an opaque copy: a caller that runs this body in a loop (the
+    // grouped kernel) would otherwise keep every lane-dependent address it derives live
+    // across the whole loop
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int KH = K >> 1, G = K >> 4, nchunk = K >> 4;
     // the work is a sequence of steps (tile t, batch gb): batch gb covers groups
-    // 256*gb .. 256*gb + 255 of each of the tile's rows; tile t covers rows
+    // 64*NB*gb .. 64*NB*(gb + 1) - 1 of each of the tile's rows; tile t covers rows
     // 4R*(tile0 + t*tstride) ..; wave w takes R consecutive rows of it
-    const int nbt = (nchunk + 64 * GV_BATCH - 1) / (64 * GV_BATCH);
+    static_assert(NB == 3 || NB == 4, "3 or 4 groups per lane");
+    constexpr int BG = 64 * NB;   // groups per batch
+    const int nbt = (nchunk + BG - 1) / BG;
     const int nsteps = ntile * nbt;
-    auto issue = [&](Batch<R>& dst, int step) __attribute__((always_inline)) {
-        step = min(step, nsteps - 1);   // past the end: a harmless reload of the last step
-        const int t = step / nbt, gb = step - t * nbt;
+    // a step as (tile, batch), advanced by counting (no divisions; uniform, scalar)
+    struct Pos {
+        int t, gb;
+    };
+    auto advance = [&](Pos p) __attribute__((always_inline)) {
+        return p.gb + 1 == nbt ? Pos{p.t + 1, 0} : Pos{p.t, p.gb + 1};
+    };
+    auto issue = [&](Batch<R, NB>& dst, Pos p) __attribute__((always_inline)) {
+        if (p.t >= ntile) p = Pos{ntile - 1, nbt - 1};   // past the end: a harmless reload of the last step
+        const int t = p.t, gb = p.gb;
         const uint8_t* qr[R];
         const uint8_t* sr[R];
 #pragma unroll
@@ -311,7 +357,7 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
             qr[r] = qp + (int64_t)n * KH;
             sr[r] = srel + (int64_t)n * G;
         }
-        load_batch<R>(dst, qr, sr, 4 * lane + gb * 64 * GV_BATCH, nchunk);
+        load_batch<R, NB>(dst, qr, sr, NB * lane + gb * BG, nchunk);
         if constexpr (CARRY) {
             // the epilogue operands travel with the batch: loaded at the tile's end, after
             // the next prefetch, the wait for them would drain that prefetch at every tile
@@ -327,33 +373,33 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
     };
 
     float* xs_w = reinterpret_cast<float*>(act + MM * SLAB);   // the rows' activation scales
-    Batch<R> bA, bB;
+    Batch<R, NB> bA, bB;
     if constexpr (FUSED) {
         // the first rotation inputs, then (after a compiler barrier that keeps this issue
         // order) the first weight batch: the rotation waits only for its own loads
         const RotIn first0 = rot_first_job<MM>(x, K, 0), first1 = rot_first_job<MM>(x, K, 1);
         __builtin_amdgcn_sched_barrier(0);
-        issue(bA, 0);
+        issue(bA, Pos{0, 0});
         float cb[16];
 #pragma unroll
         for (int c = 0; c < 16; ++c) cb[c] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(codebook[c])));
-        build_level_table_regs(lut, cb, threadIdx.x, GV_THREADS);
+        build_level_table_regs(lut, cb, tid, GV_THREADS);
         double* tbuf = reinterpret_cast<double*>(act + MM * SLAB + 32);
-        rotate_quant_to_lds<MM, LONGK>(act, xs_w, tbuf, reinterpret_cast<float*>(tbuf + ROTQ_TBUF_DOUBLES), x, K, qmax,
+        rotate_quant_to_lds<MM, NB, LONGK>(act, xs_w, tbuf, reinterpret_cast<float*>(tbuf + ROTQ_TBUF_DOUBLES), x, K, qmax,
                                 first0, first1, xq_out, xs_out);
     } else {
         // activation loads first, then the first weight batch: the wait before the
         // activation stores leaves the weight loads outstanding while the level table
         // is built from the codebook (uniform loads)
         const int cols0 = K < SLAB ? K : SLAB;
-        const float xsv = xs[min((int)threadIdx.x, MM - 1)];
-        stage_acts<MM>(act, xq, K, 0, cols0, [&]() __attribute__((always_inline)) { issue(bA, 0); });
+        const float xsv = xs[min(tid, MM - 1)];
+        stage_acts<MM, NB>(act, xq, K, 0, cols0, tid, [&]() __attribute__((always_inline)) { issue(bA, Pos{0, 0}); });
         // scales in LDS: a lane-dependent index into a register array would put it in scratch memory
-        if (threadIdx.x < MM) xs_w[threadIdx.x] = xsv;
+        if (tid < MM) xs_w[tid] = xsv;
         float cb[16];
 #pragma unroll
         for (int c = 0; c < 16; ++c) cb[c] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(codebook[c])));
-        build_level_table_regs(lut, cb, threadIdx.x, GV_THREADS);
+        build_level_table_regs(lut, cb, tid, GV_THREADS);
     }
     __syncthreads();
 
@@ -367,42 +413,42 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
     // can count the loads in flight), multiply-accumulate `cur`, and finish the tile after
     // its last batch.  `live` is false only for the padding step of an odd count, which
     // only issues its (harmless) prefetch.
-    auto body = [&](int step, const Batch<R>& cur, Batch<R>& nxt, bool live, auto one_slab, auto prefetch)
+    auto body = [&](Pos pos, const Batch<R, NB>& cur, Batch<R, NB>& nxt, bool live, auto one_slab, auto prefetch)
                     __attribute__((always_inline)) {
         constexpr bool ONE = decltype(one_slab)::value;
-        if (decltype(prefetch)::value) issue(nxt, step + 1);
+        if (decltype(prefetch)::value) issue(nxt, advance(pos));
         if (!live) return;   // the padding step only keeps the load count even
-        const int t = step / nbt, gb = step - t * nbt;
+        const int t = pos.t, gb = pos.gb;
         if (gb == 0) {
 #pragma unroll
             for (int i = 0; i < R * MM; ++i) acc[i] = 0;
         }
         if (!ONE) {
-            const int k0 = (gb * 64 * GV_BATCH * 16 / SLAB) * SLAB;
+            const int k0 = (gb * BG * 16 / SLAB) * SLAB;   // NB = 4 here: a batch never straddles slabs
             if (k0 != slab_k0) {                 // other slab of activations (uniform)
                 slab_k0 = k0;
                 const int cols = K - slab_k0 < SLAB ? K - slab_k0 : SLAB;
                 __syncthreads();
-                stage_acts<MM>(act, xq, K, slab_k0, cols, []() {});
+                stage_acts<MM, NB>(act, xq, K, slab_k0, cols, tid, []() {});
                 __syncthreads();
             }
         }
-        const int jb = 4 * lane + gb * 64 * GV_BATCH;   // the lane's first group of the batch
-        if (jb < nchunk) {                                // all 4 groups, or none (nchunk % 16 == 0)
-            // chunks c0 + u (c0 = a multiple of 4) sit at act_chunk(c0) ^ u: one address
-            // per batch, an xor per group
-            const int a0 = act_chunk(jb - (slab_k0 >> 4)) * 16;
+        const int jb = NB * lane + gb * BG;   // the lane's first group of the batch
+        if (jb < nchunk) {                     // all NB groups, or none
+            // NB = 4: chunks c0 + u (c0 = a multiple of 4) sit at act_chunk(c0) ^ u, one
+            // address per batch and an xor per group; NB = 3: at c0 + u
+            const int a0 = act_chunk<NB>(jb - (slab_k0 >> 4)) * 16;
 #pragma unroll
-            for (int u = 0; u < GV_BATCH; ++u) {
+            for (int u = 0; u < NB; ++u) {
                 uint4 a[MM];
+                const int au = NB == 4 ? (a0 ^ (16 * u)) : a0 + 16 * u;
 #pragma unroll
-                for (int m = 0; m < MM; ++m) a[m] = *reinterpret_cast<const uint4*>(act + m * SLAB + (a0 ^ (16 * u)));
+                for (int m = 0; m < MM; ++m) a[m] = *reinterpret_cast<const uint4*>(act + m * SLAB + au);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const uint4 tt = lut4[(cur.s[r] >> (8 * u)) & 0xFFu];
-                    const uint4 qq = cur.q[u >> 1][r];
-                    const uint2 d0 = decode_split((u & 1) ? qq.z : qq.x, tt, id),
-                                d1 = decode_split((u & 1) ? qq.w : qq.y, tt, id);
+                    const uint2 d0 = decode_split(cur.q[r][2 * u], tt, id),
+                                d1 = decode_split(cur.q[r][2 * u + 1], tt, id);
 #pragma unroll
                     for (int m = 0; m < MM; ++m) {
                         int32_t sacc = acc[r * MM + m];
@@ -435,7 +481,7 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
                 for (int i = 0; i < half; ++i) {
                     const int32_t d = (v[i] ^ v[i + half]) & hm;
                     const int32_t keep = v[i] ^ d, send = v[i + half] ^ d;
-                    v[i] = keep + lane_xor(send, o);
+                    v[i] = keep + lane_xor(send, o, lane);
                 }
             }
             // then the sum over the 64 >> L lanes that share a value: within a 16-lane row by
@@ -446,8 +492,8 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
             if constexpr (G >= 4) v[0] += __builtin_amdgcn_update_dpp(0, v[0], 0x4E, 0xF, 0xF, false);
             if constexpr (G >= 8) v[0] += __builtin_amdgcn_update_dpp(0, v[0], 0x141, 0xF, 0xF, false);
             if constexpr (G >= 16) v[0] += __builtin_amdgcn_update_dpp(0, v[0], 0x140, 0xF, 0xF, false);
-            if constexpr (G >= 32) v[0] += lane_xor(v[0], 16);
-            if constexpr (G >= 64) v[0] += lane_xor(v[0], 32);
+            if constexpr (G >= 32) v[0] += lane_xor(v[0], 16, lane);
+            if constexpr (G >= 64) v[0] += lane_xor(v[0], 32, lane);
 
             const int n0 = ((tile0 + t * tstride) * WAVES + wave) * R;
             const int idx = lane >> (6 - L);
@@ -486,17 +532,20 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
         }
     };
     auto run = [&](auto one_slab) __attribute__((always_inline)) {
+        Pos pos{0, 0};
         for (int step = 0; step < nsteps; step += 2) {   // ping-pong: no register copies
-            body(step, bA, bB, true, one_slab, std::true_type{});
-            body(step + 1, bB, bA, step + 1 < nsteps, one_slab, std::true_type{});
+            body(pos, bA, bB, true, one_slab, std::true_type{});
+            pos = advance(pos);
+            body(pos, bB, bA, step + 1 < nsteps, one_slab, std::true_type{});
+            pos = advance(pos);
         }
     };
-    if (nsteps == 1) body(0, bA, bB, true, std::true_type{}, std::false_type{});   // one tile, one batch
+    if (nsteps == 1) body(Pos{0, 0}, bA, bB, true, std::true_type{}, std::false_type{});   // one tile, one batch
     else if (FUSED || K <= SLAB) run(std::true_type{});
-    else if constexpr (!FUSED) run(std::false_type{});
+    else if constexpr (!FUSED && NB == 4) run(std::false_type{});   // 3 groups per lane: one slab only
 }
 
-template <int MM, int R>
+template <int MM, int R, int NB>
 __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(const int8_t* __restrict__ xq, const float* __restrict__ xs,
                                                           const uint8_t* __restrict__ qp,
                                                           const uint8_t* __restrict__ srel,
@@ -505,11 +554,11 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_kernel(const int8_t* __restri
                                                           const float* __restrict__ bias, int N, int K,
                                                           int out_type, void* __restrict__ out) {
     // carrying the epilogue operands measured faster for several rows, slower for one
-    gemv_body<MM, R, false, false, (MM > 1)>(xq, xs, qp, srel, codebook, ws, bias, N, K, out_type, out, blockIdx.x, 1,
-                                             1);
+    gemv_body<MM, R, NB, false, false, (MM > 1)>(xq, xs, qp, srel, codebook, ws, bias, N, K, out_type, out, blockIdx.x,
+                                                 1, 1);
 }
 
-template <int MM, int R, bool LONGK>
+template <int MM, int R, int NB, bool LONGK>
 __global__ __launch_bounds__(GV_THREADS) void gemv_act_kernel(const uint16_t* __restrict__ x, int qmax,
                                                               const uint8_t* __restrict__ qp,
                                                               const uint8_t* __restrict__ srel,
@@ -519,71 +568,115 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_act_kernel(const uint16_t* __
                                                               int out_type, void* __restrict__ out,
                                                               int8_t* __restrict__ xq_out, float* __restrict__ xs_out) {
     const bool first = blockIdx.x == 0;   // one block writes the prepared activations out
-    gemv_body<MM, R, true, LONGK>(nullptr, nullptr, qp, srel, codebook, ws, bias, N, K, out_type, out, blockIdx.x, 1, 1, x,
-                           qmax, first ? xq_out : nullptr, first ? xs_out : nullptr);
+    gemv_body<MM, R, NB, true, LONGK>(nullptr, nullptr, qp, srel, codebook, ws, bias, N, K, out_type, out, blockIdx.x, 1,
+                                      1, x, qmax, first ? xq_out : nullptr, first ? xs_out : nullptr);
 }
 
 // Several independent layers (same M) in one launch: block b works on the layer whose
 // range [first[l], first[l+1]) of block ids holds b, as block b - first[l] of it, on
 // every nblk-th row tile of the layer (the level table and the activations are staged
 // once per block; the first loads of a tile are issued during the last batch of the
-// previous one).  The layer table travels in the kernel arguments.
+// previous one).  The blocks running at one time thus read neighbouring rows of one
+// layer.  The layer table travels in the kernel arguments (about 5.5 KB), with each
+// layer's groups per lane and batch (gemv_nb).
 struct GroupArgs {
     int count;
     int first[GEMV_GROUP_MAX + 1];
+    uint8_t nb[GEMV_GROUP_MAX];
     w4a8_gemv_layer layer[GEMV_GROUP_MAX];
 };
 
 // for one activation row, at most 128 registers (4 waves per SIMD, measured faster than 3)
 template <int MM, int R>
 __global__ __launch_bounds__(GV_THREADS, MM == 1 ? 4 : 1) void gemv_grouped_kernel(const GroupArgs args, int out_type) {
+    // the layer: the last l with first[l] <= block id (binary search, uniform)
     int l = 0;
-    while (l + 1 < args.count && (int)blockIdx.x >= args.first[l + 1]) ++l;   // uniform: a few steps
+    for (int hi = args.count - 1; l < hi;) {
+        const int mid = (l + hi + 1) >> 1;
+        if (args.first[mid] <= (int)blockIdx.x) l = mid;
+        else hi = mid - 1;
+    }
     const w4a8_gemv_layer& L = args.layer[l];
     const int per_tile = (GV_THREADS / 64) * R;
     const int tiles = (int)((L.N + per_tile - 1) / per_tile);
-    // the layer's nblk blocks take its tiles round robin (block bl: tiles bl, bl + nblk, ...), so
-    // the blocks running at one time read neighbouring rows
     const int nblk = args.first[l + 1] - args.first[l], bl = (int)blockIdx.x - args.first[l];
     const int ntile = (tiles - bl + nblk - 1) / nblk;
-    gemv_body<MM, R, false, false, true>(L.xq, L.xs, L.qpacked, L.srel, L.codebook, L.s_channel, L.bias, (int)L.N,
-                                         (int)L.K, out_type, L.out, bl, ntile, nblk);
+    if (args.nb[l] == 3)   // block-uniform
+        gemv_body<MM, R, 3, false, false, true>(L.xq, L.xs, L.qpacked, L.srel, L.codebook, L.s_channel, L.bias,
+                                                (int)L.N, (int)L.K, out_type, L.out, bl, ntile, nblk);
+    else
+        gemv_body<MM, R, 4, false, false, true>(L.xq, L.xs, L.qpacked, L.srel, L.codebook, L.s_channel, L.bias,
+                                                (int)L.N, (int)L.K, out_type, L.out, bl, ntile, nblk);
 }
 
 // rows per wave: 2 when that still gives >= 2048 waves (8 per compute unit), else 1
 // (4 rows per wave would need so many registers that few waves fit per SIMD)
 int rows_per_wave(int64_t rows) { return (rows + 1) / 2 >= 2048 ? 2 : 1; }
 
+// Blocks of gemv_grouped_kernel<MM, R> that are resident on one compute unit at a time
+// (from the runtime's occupancy calculation; cached, the same for every gfx950 device).
+template <int MM, int R>
+int grouped_blocks_per_cu() {
+    static std::atomic<int> cached{0};
+    int v = cached.load(std::memory_order_relaxed);
+    if (v == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_grouped_kernel<MM, R>, GV_THREADS,
+                                                         gemv_lds_bytes(MM, false)) != hipSuccess || n < 1)
+            n = 1;
+        cached.store(n, std::memory_order_relaxed);
+        v = n;
+    }
+    return v;
+}
+
 template <int MM>
 hipError_t launch_gemv_grouped_m(const w4a8_gemv_layer* layers, int count, int out_type, hipStream_t stream) {
-    int64_t rows = 0, steps = 0;
+    int64_t rows = 0;
     for (int i = 0; i < count; ++i) rows += layers[i].N;
     const int R = out_type == 3 ? 2 : rows_per_wave(rows), per_tile = (GV_THREADS / 64) * R;   // SwiGLU pairs rows
-    // a tile of a layer with K columns takes nbt(K) steps of one weight batch each; blocks
-    // get about the same number of steps (not tiles), so that layers of different K end
-    // together, and the set is cut into about GV_GROUP_BLOCKS blocks (a few rounds over the
-    // chip: fewer, longer blocks leave a tail, more, shorter ones repeat the set-up)
-    auto tiles_of = [&](int i) { return (layers[i].N + per_tile - 1) / per_tile; };
-    auto nbt_of = [&](int i) { return (layers[i].K / 16 + 64 * GV_BATCH - 1) / (64 * GV_BATCH); };
-    for (int i = 0; i < count; ++i) steps += tiles_of(i) * nbt_of(i);
-    const int64_t per_block = steps / GV_GROUP_BLOCKS > 1 ? steps / GV_GROUP_BLOCKS : 1;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int64_t slots = (int64_t)cus * (R == 2 ? grouped_blocks_per_cu<MM, 2>() : grouped_blocks_per_cu<MM, 1>());
+    // A tile of layer i costs cost(i) (its weight batches of 3 or 4 groups per lane, plus about
+    // one for the epilogue).  Each launch is cut into at most GV_ROUNDS rounds of `slots`
+    // blocks of about equal cost: the blocks of a layer take its tiles round robin, and the
+    // block counts are rounded down, so no block starts in a partial last round.
+    auto nb_of = [&](const w4a8_gemv_layer& L) { return gemv_nb((int)L.K, slab_cols(MM)); };
+    auto tiles_of = [&](const w4a8_gemv_layer& L) { return (L.N + per_tile - 1) / per_tile; };
+    auto cost_of = [&](const w4a8_gemv_layer& L) {
+        const int nb = nb_of(L);
+        return (L.K / 16 + 64 * nb - 1) / (64 * nb) * nb + 1;
+    };
     for (int base = 0; base < count; base += GEMV_GROUP_MAX) {
         GroupArgs a;
         a.count = count - base < GEMV_GROUP_MAX ? count - base : GEMV_GROUP_MAX;
+        int64_t total = 0;
+        for (int i = 0; i < a.count; ++i) total += tiles_of(layers[base + i]) * cost_of(layers[base + i]);
+        const int64_t target = GV_ROUNDS * slots;
         a.first[0] = 0;
         for (int i = 0; i < a.count; ++i) {
-            a.layer[i] = layers[base + i];
-            const int64_t tpb = per_block / nbt_of(base + i) > 1 ? per_block / nbt_of(base + i) : 1;
-            a.first[i + 1] = a.first[i] + (int)((tiles_of(base + i) + tpb - 1) / tpb);
+            const w4a8_gemv_layer& L = layers[base + i];
+            a.layer[i] = L;
+            a.nb[i] = (uint8_t)nb_of(L);
+            const int64_t t = tiles_of(L);
+            int64_t n = t * cost_of(L) * target / total;
+            n = n < 1 ? 1 : n > t ? t : n;
+            a.first[i + 1] = a.first[i] + (int)n;
         }
-        for (int i = a.count; i < GEMV_GROUP_MAX; ++i) a.first[i + 1] = a.first[a.count];
+        for (int i = a.count; i < GEMV_GROUP_MAX; ++i) {
+            a.first[i + 1] = a.first[a.count];
+            a.nb[i] = 4;
+        }
         const size_t lds = gemv_lds_bytes(MM, false);
         const dim3 g(a.first[a.count]), b(GV_THREADS);
         if (R == 2)
             hipLaunchKernelGGL((gemv_grouped_kernel<MM, 2>), g, b, lds, stream, a, out_type);
         else
             hipLaunchKernelGGL((gemv_grouped_kernel<MM, 1>), g, b, lds, stream, a, out_type);
-        const hipError_t e = hipGetLastError();
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -598,12 +691,16 @@ hipError_t launch_gemv_m(const int8_t* xq, const float* xs, const uint8_t* qp, c
     const int blocks = (N + waves_per_block * R - 1) / (waves_per_block * R);
     const size_t lds = gemv_lds_bytes(MM, false);
     const dim3 g(blocks), b(GV_THREADS);
-    if (R == 2)
-        hipLaunchKernelGGL((gemv_kernel<MM, 2>), g, b, lds, stream, xq, xs, qp, srel, codebook, ws, bias, N, K,
-                           out_type, out);
-    else
-        hipLaunchKernelGGL((gemv_kernel<MM, 1>), g, b, lds, stream, xq, xs, qp, srel, codebook, ws, bias, N, K,
-                           out_type, out);
+    const int nb = gemv_nb(K, slab_cols(MM));
+#define GV_LAUNCH(RR, NBV)                                                                                           \
+    hipLaunchKernelGGL((gemv_kernel<MM, RR, NBV>), g, b, lds, stream, xq, xs, qp, srel, codebook, ws, bias, N, K, \
+                       out_type, out)
+    if (R == 2) {
+        if (nb == 3) GV_LAUNCH(2, 3); else GV_LAUNCH(2, 4);
+    } else {
+        if (nb == 3) GV_LAUNCH(1, 3); else GV_LAUNCH(1, 4);
+    }
+#undef GV_LAUNCH
     return hipGetLastError();
 }
 
@@ -616,18 +713,23 @@ hipError_t launch_gemv_act_m(const uint16_t* x, int qmax, const uint8_t* qp, con
     const int blocks = (N + waves_per_block * R - 1) / (waves_per_block * R);
     const size_t lds = gemv_lds_bytes(MM, true);
     const dim3 g(blocks), b(GV_THREADS);
-#define GV_ACT_LAUNCH(RR, LL)                                                                               \
-    hipLaunchKernelGGL((gemv_act_kernel<MM, RR, LL>), g, b, lds, stream, x, qmax, qp, srel, codebook, ws, bias, N, \
-                       K, out_type, out, xq_out, xs_out)
+    const int nb = gemv_nb(K, slab_cols(MM));
+#define GV_ACT_LAUNCH(RR, NBV, LL)                                                                               \
+    hipLaunchKernelGGL((gemv_act_kernel<MM, RR, NBV, LL>), g, b, lds, stream, x, qmax, qp, srel, codebook, ws, bias, \
+                       N, K, out_type, out, xq_out, xs_out)
+#define GV_ACT_NB(RR, LL)                  \
+    if (nb == 3) GV_ACT_LAUNCH(RR, 3, LL); \
+    else GV_ACT_LAUNCH(RR, 4, LL)
     if constexpr (slab_cols(MM) > 4096) {
         if (K > 4096) {
-            if (R == 2) GV_ACT_LAUNCH(2, true);
-            else GV_ACT_LAUNCH(1, true);
+            if (R == 2) { GV_ACT_NB(2, true); }
+            else { GV_ACT_NB(1, true); }
             return hipGetLastError();
         }
     }
-    if (R == 2) GV_ACT_LAUNCH(2, false);
-    else GV_ACT_LAUNCH(1, false);
+    if (R == 2) { GV_ACT_NB(2, false); }
+    else { GV_ACT_NB(1, false); }
+#undef GV_ACT_NB
 #undef GV_ACT_LAUNCH
     return hipGetLastError();
 }

@@ -188,8 +188,8 @@ int64_t w4a8_gemv_act_max_k(int64_t M);
 
 /*
  * w4a8_gemv_grouped -- w4a8_gemv for several independent layers in as few launches as
- * possible (32 layers per launch): the decode path of ai-toolkit w4a8_gemv_kernel for
- * each layer, with the per-launch latency paid once per 32 layers instead of once per
+ * possible (64 layers per launch): the decode path of ai-toolkit w4a8_gemv_kernel for
+ * each layer, with the per-launch latency paid once per 64 layers instead of once per
  * layer.  Every layer's output is bit-identical to a w4a8_gemv call on it.
  *
  *   layers    in   HOST array of `count` descriptors (read during the call only); each

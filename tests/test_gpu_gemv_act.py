@@ -40,7 +40,9 @@ def two_call(x, layer, out_dtype):
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8])
-@pytest.mark.parametrize("n,k", [(37, 256), (1000, 3072), (4096, 4096), (130, 8192), (300, 16384), (64, 32768)])
+# K = 768, 3072, 9216: 3 groups per lane and batch (768: lanes past the row); the others 4
+@pytest.mark.parametrize("n,k", [(37, 256), (257, 768), (1000, 3072), (4096, 4096), (130, 8192), (200, 9216),
+                                 (300, 16384), (64, 32768)])
 def test_gemv_act_equals_rotate_quant_then_gemv(m, n, k):
     if k > B.gemv_act_max_k(m):
         pytest.skip(f"K={k} is above the on-chip size for M={m}")

@@ -2,7 +2,7 @@
 binding): every layer's output must be bit-identical to w4a8_gemv on that layer,
 which the single-layer tests pin to the oracle; one layer of each decode-set shape
 is also checked against the oracle directly.  Covers mixed shapes, more layers
-than one launch holds (32), M = 1..8, bias / no bias, and the three output types."""
+than one launch holds (64), M = 1..8, bias / no bias, and the three output types."""
 
 import numpy as np
 import pytest
@@ -38,9 +38,10 @@ def as_bits(t):
 @pytest.mark.parametrize("m", [1, 3, 8])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32, torch.int32])
 def test_grouped_equals_single_gemv(m, out_dtype):
-    shapes = [(37, 256), (1000, 3072), (130, 12288), (4096, 4096), (257, 768)]
+    # 3 groups per lane and batch for K = 3072, 768 and (M <= 2) 9216, 4 for the others
+    shapes = [(37, 256), (1000, 3072), (130, 12288), (4096, 4096), (257, 768), (300, 9216)]
     items = []
-    for i in range(40):                                  # 40 layers: two launches
+    for i in range(70):                                  # 70 layers: two launches
         n, k = shapes[i % len(shapes)]
         layer = layer_from_bytes(n, k, seed=synth.seed_for(11, i, synth.ROLE_BYTES), with_bias=i % 3 == 0)
         xq, xs = acts(m, k, synth.seed_for(11, i, synth.ROLE_ACT))

@@ -256,7 +256,10 @@ def test_gemm_int32_exact_and_epilogue_bitwise(m, n, k):
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("n,k", [(4096, 4096), (37, 256), (1000, 3072), (130, 12288)])
+# K = 768, 1536, 3072 and (M <= 2) 9216 take 3 groups per lane and batch, the others 4;
+# 9216 and 12288 span several activation slabs for the larger M
+@pytest.mark.parametrize("n,k", [(4096, 4096), (37, 256), (257, 768), (64, 1536), (1000, 3072), (300, 9216),
+                                 (130, 12288)])
 def test_gemv_exact_and_equal_to_gemm(m, n, k):
     say("gemv", m, n, k)
     xq, xs = random_xq(m, k, seed=100 + m + k)
