@@ -495,14 +495,24 @@ def main():
     device = "cuda:0"
     torch.cuda.set_device(0)
 
+    t_start = time.perf_counter()
+
+    def done(part):   # a progress line on stderr as each part ends (the JSON line stays alone on stdout)
+        print(f"bench: {part} done at {time.perf_counter() - t_start:.1f} s", file=sys.stderr, flush=True)
+
     pre = bench_prefill(args, torch, B, device)
+    done("prefill step")
     gemv = None if args.no_gemv else bench_gemv(args, torch, B, device)
     floor = None if args.no_gemv else launch_floor(args, torch, B)
     decode_layers, decode_set = (None, None) if args.no_gemv else bench_decode_set(args, torch, B, device)
+    done("decode GEMVs")
     prefill_shapes = None if args.no_prefill_shapes else bench_prefill_shapes(args, torch, B, device, decode_layers)
     del decode_layers
+    done("prefill shapes")
     training = None if args.no_training else bench_training(args, torch, B, device)
+    done("training-path kernels")
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre)
+    done("cpu baseline")
 
     tops = pre["ops"] / pre["wall_s"] / 1e12
     gemm_tops = pre["ops"] / (pre["gemm_ms"] * 1e-3) / 1e12

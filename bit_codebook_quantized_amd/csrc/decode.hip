@@ -30,8 +30,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(const uint8_t* __re
         const uint4 p = *reinterpret_cast<const uint4*>(qp + c * 16);
         const uint32_t sb = *reinterpret_cast<const uint16_t*>(srel + c * 2);
         const uint4 t0 = lut4[sb & 0xFFu], t1 = lut4[sb >> 8];
-        const uint2 d0 = decode8(p.x, t0), d1 = decode8(p.y, t0);
-        const uint2 d2 = decode8(p.z, t1), d3 = decode8(p.w, t1);
+        const uint2 d0 = decode8(p.x, t0, 0x03020100u), d1 = decode8(p.y, t0, 0x03020100u);
+        const uint2 d2 = decode8(p.z, t1, 0x03020100u), d3 = decode8(p.w, t1, 0x03020100u);
         uint4* o = reinterpret_cast<uint4*>(w8 + c * 32);
         o[0] = make_uint4(d0.x, d0.y, d1.x, d1.y);
         o[1] = make_uint4(d2.x, d2.y, d3.x, d3.y);

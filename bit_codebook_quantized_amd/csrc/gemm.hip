@@ -132,6 +132,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / WN, wn = wave % WN;
+    const uint32_t id = opaque_identity_selector();   // the decode's merge selector base
     const int ntiles = tiles_m * tiles_n;
     int pid = blockIdx.x;
     if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);
@@ -212,8 +213,8 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     };
     // group g (0/1) of a piece: 16 codes -> 16 int8 levels, one fragment of the weight buffer
     auto decode_group = [&](const Piece& p, int g, int buf) __attribute__((always_inline)) {
-        const uint2 d0 = decode8(g ? p.x.z : p.x.x, g ? p.t1 : p.t0);
-        const uint2 d1 = decode8(g ? p.x.w : p.x.y, g ? p.t1 : p.t0);
+        const uint2 d0 = decode8(g ? p.x.z : p.x.x, g ? p.t1 : p.t0, id);
+        const uint2 d1 = decode8(g ? p.x.w : p.x.y, g ? p.t1 : p.t0, id);
         *reinterpret_cast<v4u*>(Bs + buf * B_STAGE + 128 * p.n + 16 * swz(p.n, cpair + g)) =
             v4u{d0.x, d0.y, d1.x, d1.y};
     };

@@ -62,7 +62,7 @@ __device__ __forceinline__ uint4 level_row(const float (&cb)[16], float s) {
 // One group's 16 weights (codes q, 8 bytes) as fp32(level * s_channel): a byte-permute
 // decode against the level row, no per-weight codebook reads.
 __device__ __forceinline__ void decode_group_f32(uint2 q, uint4 t, float sch, float (&w)[16]) {
-    const uint2 d0 = decode8(q.x, t), d1 = decode8(q.y, t);
+    const uint2 d0 = decode8(q.x, t, 0x03020100u), d1 = decode8(q.y, t, 0x03020100u);
     const uint32_t d[4] = {d0.x, d0.y, d1.x, d1.y};
 #pragma unroll
     for (int k = 0; k < 16; ++k) w[k] = __fmul_rn((float)(int8_t)(uint8_t)(d[k >> 2] >> (8 * (k & 3))), sch);

@@ -72,29 +72,11 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// Decode the 8 codes of one packed dword (byte i = code 2i | code 2i+1 << 4)
-// against the 16-level row t = {L0..3, L4..7, L8..11, L12..15}.
-// Returns the 8 int8 levels in natural column order: .x = k0..k3, .y = k4..k7.
-__device__ __forceinline__ uint2 decode8(uint32_t x, uint4 t) {
-    const uint32_t se = x & 0x07070707u;           // even codes, low 3 bits
-    const uint32_t so = (x >> 4) & 0x07070707u;    // odd codes, low 3 bits
-    const uint32_t lo_e = perm(t.y, t.x, se), hi_e = perm(t.w, t.z, se);
-    const uint32_t lo_o = perm(t.y, t.x, so), hi_o = perm(t.w, t.z, so);
-    // bit 3 of each code picks the upper half of the table: selector i or i + 4
-    const uint32_t me = ((x >> 1) & 0x04040404u) | 0x03020100u;
-    const uint32_t mo = ((x >> 5) & 0x04040404u) | 0x03020100u;
-    const uint32_t re = perm(hi_e, lo_e, me);      // columns 0, 2, 4, 6
-    const uint32_t ro = perm(hi_o, lo_o, mo);      // columns 1, 3, 5, 7
-    uint2 r;
-    r.x = perm(ro, re, 0x05010400u);
-    r.y = perm(ro, re, 0x07030602u);
-    return r;
-}
-
 // The 8 codes of one packed dword (byte i = code 2i | code 2i+1 << 4) against the
 // 16-level row t = {L0..3, L4..7, L8..11, L12..15}: .x = the levels of columns 0, 2, 4, 6,
 // .y = those of columns 1, 3, 5, 7.  `id` is 0x03020100 held in a register (so the merge
-// selector is one and-or).
+// selector is one and-or; as a literal it would take an and and an or, since an
+// instruction holds one literal).
 __device__ __forceinline__ uint2 decode_split(uint32_t x, uint4 t, uint32_t id) {
     const uint32_t se = x & 0x07070707u;           // even codes, low 3 bits
     const uint32_t so = (x >> 4) & 0x07070707u;    // odd codes, low 3 bits
@@ -104,6 +86,19 @@ __device__ __forceinline__ uint2 decode_split(uint32_t x, uint4 t, uint32_t id) 
     const uint32_t me = ((x >> 1) & 0x04040404u) | id;
     const uint32_t mo = ((x >> 5) & 0x04040404u) | id;
     return uint2{perm(hi_e, lo_e, me), perm(hi_o, lo_o, mo)};
+}
+
+// The same 8 levels in natural column order: .x = k0..k3, .y = k4..k7.
+__device__ __forceinline__ uint2 decode8(uint32_t x, uint4 t, uint32_t id) {
+    const uint2 s = decode_split(x, t, id);
+    return uint2{perm(s.y, s.x, 0x05010400u), perm(s.y, s.x, 0x07030602u)};
+}
+
+// 0x03020100 (the identity byte selector) in a register the compiler cannot fold
+__device__ __forceinline__ uint32_t opaque_identity_selector() {
+    uint32_t id = 0x03020100u;
+    asm volatile("" : "+v"(id));
+    return id;
 }
 
 // fp32(x / s) for a divisor s > 0 used many times, with inv = fp64(1 / s): the fp64
