@@ -309,7 +309,7 @@ __device__ __forceinline__ void rotate_quant_to_lds(uint8_t* act, float* xs_lds,
 // rotate_quant_to_lds; K <= slab_cols(MM)) instead of xq / xs.
 // CARRY: the tile's channel scales and biases are loaded with each batch (for blocks that
 // walk several tiles); otherwise they are loaded once, in the tile's epilogue.
-template <int MM, int R, int NB, bool FUSED = false, bool LONGK = false, bool CARRY = false>
+template <int MM, int R, int NB, bool FUSED = false, bool LONGK = false, bool CARRY = false, bool GROUPED = false>
 __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const float* __restrict__ xs,
                                           const uint8_t* __restrict__ qp, const uint8_t* __restrict__ srel,
                                           const float* __restrict__ codebook, const float* __restrict__ ws,
@@ -325,11 +325,12 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
     constexpr int WAVES = GV_THREADS / 64;
 
     // the wave index as a uniform value, so row-dependent scalars use scalar loads
-    // the thread index through an opaque copy: a caller that runs this body in a loop (the
-    // grouped kernel) would otherwise keep every lane-dependent address it derives live
-    // across the whole loop
+    // GROUPED (two instantiations of this body in one kernel): the thread index through an
+    // opaque copy, so the compiler recomputes the lane-dependent addresses it derives where
+    // they are used instead of keeping them all live (which spilled); the single-layer
+    // kernels measured faster with the plain index
     int tid = (int)threadIdx.x;
-    asm volatile("" : "+v"(tid));
+    if constexpr (GROUPED) asm volatile("" : "+v"(tid));
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int KH = K >> 1, G = K >> 4, nchunk = K >> 4;
     // the work is a sequence of steps (tile t, batch gb): batch gb covers groups
@@ -545,8 +546,10 @@ __device__ __forceinline__ void gemv_body(const int8_t* __restrict__ xq, const f
     else if constexpr (!FUSED && NB == 4) run(std::false_type{});   // 3 groups per lane: one slab only
 }
 
+// for one activation row, at most 128 registers (4 waves per SIMD; 131 registers, 3 waves,
+// measured 0.9 us slower at N = K = 4096)
 template <int MM, int R, int NB>
-__global__ __launch_bounds__(GV_THREADS) void gemv_kernel(const int8_t* __restrict__ xq, const float* __restrict__ xs,
+__global__ __launch_bounds__(GV_THREADS, MM == 1 ? 4 : 1) void gemv_kernel(const int8_t* __restrict__ xq, const float* __restrict__ xs,
                                                           const uint8_t* __restrict__ qp,
                                                           const uint8_t* __restrict__ srel,
                                                           const float* __restrict__ codebook,
@@ -602,10 +605,10 @@ __global__ __launch_bounds__(GV_THREADS, MM == 1 ? 4 : 1) void gemv_grouped_kern
     const int nblk = args.first[l + 1] - args.first[l], bl = (int)blockIdx.x - args.first[l];
     const int ntile = (tiles - bl + nblk - 1) / nblk;
     if (args.nb[l] == 3)   // block-uniform
-        gemv_body<MM, R, 3, false, false, true>(L.xq, L.xs, L.qpacked, L.srel, L.codebook, L.s_channel, L.bias,
+        gemv_body<MM, R, 3, false, false, true, true>(L.xq, L.xs, L.qpacked, L.srel, L.codebook, L.s_channel, L.bias,
                                                 (int)L.N, (int)L.K, out_type, L.out, bl, ntile, nblk);
     else
-        gemv_body<MM, R, 4, false, false, true>(L.xq, L.xs, L.qpacked, L.srel, L.codebook, L.s_channel, L.bias,
+        gemv_body<MM, R, 4, false, false, true, true>(L.xq, L.xs, L.qpacked, L.srel, L.codebook, L.s_channel, L.bias,
                                                 (int)L.N, (int)L.K, out_type, L.out, bl, ntile, nblk);
 }
 
