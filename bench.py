@@ -235,6 +235,29 @@ def bench_prefill_shapes(args, torch, B, device, decode_layers=None):
     return res
 
 
+def bench_c0(args, torch, B, device):
+    """The smallest configuration, M = 16, N = K = 256 (a correctness shape, reported in us
+    only): rotate_quant_act and w4a8_gemm (M > 8), each the median of 5 trials of 100
+    back-to-back launches, and the two as one step."""
+    from bit_codebook_quantized_amd import synth
+    M, N, K = 16, 256, 256
+    w = synth.gaussian_weight_device(N, K, seed=synth.seed_for(0, 0, synth.ROLE_WEIGHT), device=device)
+    layer = make_layer(B, w)
+    x = torch.from_numpy(synth.activations(M, K, seed=synth.seed_for(0, 0, synth.ROLE_ACT))).to(
+        torch.bfloat16).to(device)
+    xq = torch.empty(M, K, dtype=torch.int8, device=device)
+    xs = torch.empty(M, dtype=torch.float32, device=device)
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=device)
+    rq = B.prepared_rotate_quant(x, xq, xs)
+    gm = B.prepared_linear("w4a8_gemm", xq, xs, layer, out)
+    sleep = int(args.sleep_cycles) // 4
+    rq_ms = median_trials(torch, [rq], 100, 5, sleep)
+    gm_ms = median_trials(torch, [gm], 100, 5, sleep)
+    step_ms = median_trials(torch, [lambda: (rq(), gm())], 100, 5, sleep)
+    return {"M": M, "N": N, "K": K, "rotate_quant_act_us": round(rq_ms * 1e3, 3),
+            "gemm_us": round(gm_ms * 1e3, 3), "step_us": round(step_ms * 1e3, 3)}
+
+
 def bench_gemv(args, torch, B, device):
     from bit_codebook_quantized_amd import synth
     N = K = 4096
@@ -254,7 +277,10 @@ def bench_gemv(args, torch, B, device):
         out = torch.empty(m, N, dtype=torch.bfloat16, device=device)
         rq = [B.prepared_rotate_quant(x, xq, xs)]
         cold = [B.prepared_linear("w4a8_gemv", xq, xs, layers[c], out) for c in range(copies)]
-        cold_ms, enq = timed_launches(torch, cold, args.gemv_launches, sleep)
+        # median of 5 trials of back-to-back launches (at least 100 each) over the 64 copies
+        per_trial = max(100, args.gemv_launches // 5)
+        _, enq = timed_launches(torch, cold, per_trial, sleep)
+        cold_ms = median_trials(torch, cold, per_trial, 5, sleep)
         warm_ms, _ = timed_launches(torch, cold[:1], 64, sleep // 4)
         rq_ms, _ = timed_launches(torch, rq, 64, sleep // 4)
         # the whole decode layer: rotate_quant_act + w4a8_gemv, and the one-launch w4a8_gemv_act
@@ -274,7 +300,7 @@ def bench_gemv(args, torch, B, device):
             layer_two_launches_us=round(two_ms * 1e3, 3),
             layer_gemv_act_us=round(act_ms * 1e3, 3),
             layer_gemv_act_weight_GBps=round(wb / (act_ms * 1e-3) / 1e9, 1),
-            host_enqueue_us=round(enq / args.gemv_launches * 1e6, 2),
+            host_enqueue_us=round(enq / per_trial * 1e6, 2),
         )
     return res
 
@@ -282,8 +308,9 @@ def bench_gemv(args, torch, B, device):
 def bench_decode_set(args, torch, B, device):
     """The 64-layer decode set at M=1 (16 layers each of 3072x3072, 9216x3072,
     12288x3072, 3072x12288; 1.02 GB of weights, four times the Infinity Cache): one
-    w4a8_gemv launch per layer, and one w4a8_gemv_grouped call (32 layers per launch)
-    for layers that are independent of each other.  GPU time of the whole set."""
+    w4a8_gemv launch per layer, and one w4a8_gemv_grouped call (one launch for all 64)
+    for layers that are independent of each other.  GPU time of the whole set, the median
+    of 10 runs."""
     from bit_codebook_quantized_amd import synth
     shapes = [(3072, 3072), (9216, 3072), (12288, 3072), (3072, 12288)]
     items, wbytes = [], 0
@@ -502,6 +529,7 @@ def main():
 
     pre = bench_prefill(args, torch, B, device)
     done("prefill step")
+    c0 = bench_c0(args, torch, B, device)
     gemv = None if args.no_gemv else bench_gemv(args, torch, B, device)
     floor = None if args.no_gemv else launch_floor(args, torch, B)
     decode_layers, decode_set = (None, None) if args.no_gemv else bench_decode_set(args, torch, B, device)
@@ -543,6 +571,7 @@ def main():
         "rotate_quant_act": {"us": round(pre["rq_ms"] * 1e3, 3),
                              "GBps": round(pre["rq_bytes"] / (pre["rq_ms"] * 1e-3) / 1e9, 1),
                              "frac_hbm": round(pre["rq_bytes"] / (pre["rq_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "c0_step": c0,
         "gemv": gemv,
         "launch_floor": floor,
         "gemv_decode_set": decode_set,

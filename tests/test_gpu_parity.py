@@ -98,6 +98,8 @@ RQ_CASES = [
     (16, 256, "normal"), (1, 4096, "normal"), (3, 4096, "normal"), (8, 4096, "outliers"),
     (37, 768, "student_t"), (33, 512, "normal"), (5, 1280, "normal"), (64, 3072, "student_t"),
     (5, 12288, "outliers"), (3, 8192, "normal"), (2, 36864, "student_t"), (17, 4352, "normal"),
+    # a full round of blocks and a ragged last one (1, 1 and 4 rows per block)
+    (2049, 4096, "outliers"), (2051, 3072, "student_t"), (8202, 1024, "normal"),
 ]
 
 
@@ -113,6 +115,23 @@ def test_rotate_quant_act_bit_exact(m, k, kind):
     ref_q, ref_s = O.rotate_quant_act(x)
     assert np.array_equal(xs.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
     assert np.array_equal(xq.cpu().numpy(), ref_q)
+
+
+def test_rotate_quant_act_full_size_rows_with_non_finite_values():
+    # the prefill activation shape with rows poisoned by an Inf or a NaN next to finite rows
+    m, k = 2048, 4096
+    x = synth.activations(m, k, seed=synth.seed_for(9, 7, 7), kind="normal")
+    x[4, 100] = np.inf
+    x[5, 3000] = np.nan
+    x[1001, 0] = -np.inf
+    say("rotate_quant_act full size, non-finite rows")
+    xq, xs = B.rotate_quant_act(bf16_dev(x))
+    rq, rs = O.rotate_quant_act(x)
+    got_s = xs.cpu().numpy()
+    assert np.array_equal(np.isnan(got_s), np.isnan(rs))
+    fin = ~np.isnan(rs)
+    assert np.array_equal(got_s[fin].view(np.uint32), rs[fin].view(np.uint32))
+    assert np.array_equal(xq.cpu().numpy(), rq)
 
 
 def test_rotate_quant_act_qmax_and_empty():
