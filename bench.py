@@ -140,13 +140,30 @@ def bench_prefill(args, torch, B, device):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
     gemm_ms = mean_ms(list(whole.values())) - mean_ms(list(part.values()))
+    # The same step launched from a HIP graph, after the timed region: 32 steps captured
+    # once (kernel nodes only, no memory-set node) and replayed.  A graph of a single step
+    # measured slower than direct launches (its replay has a fixed cost per launch), so the
+    # graph holds 32.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(32):
+            step()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // 32)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_wall = (time.perf_counter() - t0) / (32 * reps)
+    del graph
     # rotate_quant_act alone, after the timed region (an event before it in every step would
     # add a gap to the step)
     rq_ms, _ = timed_launches(torch, [rq_call], 20, int(args.sleep_cycles))
     # the GEMM alone: median of 5 trials of 100 back-to-back launches (one event pair each)
     gemm_med_ms = median_trials(torch, [gemm_call], 100, 5, int(args.sleep_cycles))
     ops = 2.0 * M * N * K
-    return dict(M=M, N=N, K=K, wall_s=wall, rq_ms=rq_ms, gemm_ms=gemm_ms, gemm_med_ms=gemm_med_ms, ops=ops,
+    return dict(M=M, N=N, K=K, wall_s=wall, graph_wall_s=graph_wall, rq_ms=rq_ms, gemm_ms=gemm_ms, gemm_med_ms=gemm_med_ms, ops=ops,
                 x_np=x_np, host=host, quant_ms=quant_ms,
                 rq_bytes=3 * M * K + 4 * M,
                 gemm_bytes=weight_bytes(N, K) + M * K + 4 * M + 2 * M * N)
@@ -552,6 +569,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(pre["wall_s"] * 1e3, 4),
+        "graph32_ms_per_step": round(pre["graph_wall_s"] * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(RQ_THREADS) void rotate_quant_kernel(const uint16_t
     // exchange between waves.  At 18.5 KB of LDS, 8 blocks share a CU.
     __shared__ __attribute__((aligned(16))) double tbuf[16 * 16 * TSTRIDE];
     static_assert(256 <= 16 * TSTRIDE * sizeof(double), "a slot's code transpose fits in its part of tbuf");
-    __shared__ float smax[16];
+    __shared__ __attribute__((aligned(16))) float smax[16];
 
     const int tid = threadIdx.x, slot = tid >> 4, l16 = tid & 15;
     uint8_t* const qb = reinterpret_cast<uint8_t*>(tbuf + slot * 16 * TSTRIDE);
@@ -97,12 +97,7 @@ __global__ __launch_bounds__(RQ_THREADS) void rotate_quant_kernel(const uint16_t
     amax = slot_max(amax);
     if (l16 == 0) smax[slot] = amax;
     __syncthreads();
-    float rmax = 0.0f;
-    if (nb <= 16) {
-        for (int s = row_local * nb; s < row_local * nb + nb && s < 16; ++s) rmax = __builtin_fmaxf(rmax, smax[s]);
-    } else {
-        for (int s = 0; s < 16; ++s) rmax = __builtin_fmaxf(rmax, smax[s]);
-    }
+    const float rmax = nb <= 16 ? slots_max(smax, row_local * nb, nb) : slots_max(smax, 0, 16);
     const float scale = row_scale(rmax, qmaxf);
     const bool poisoned = row_poisoned(rmax);
     const double inv = poisoned ? 0.0 : 1.0 / (double)scale;

@@ -103,21 +103,22 @@ __device__ __forceinline__ void rotate_block(const uint16_t* __restrict__ x, int
     rotate_loaded<WAVE_SYNC>(in, ok, slot, l16, tbuf, r);
 }
 
+// Maximum over a slot's 16 lanes (one DPP row; every lane active) of values that are >= +0
+// or +inf, never NaN (the output of block_absmax), taken on their bit patterns as unsigned
+// integers.  The row mirror pairs lane i with i ^ 15, the half-row mirror with i ^ 7, the
+// two quad permutes with i ^ 1 and i ^ 2; together they reach all 16 lanes.
 // v from another lane of the same 16-lane row (a DPP source modifier, no LDS)
 template <int CTRL>
-__device__ __forceinline__ float row_dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t row_dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
-
-// Maximum over a slot's 16 lanes (one DPP row; every lane active).  The row mirror pairs
-// lane i with i ^ 15, the half-row mirror with i ^ 7, the two quad permutes with i ^ 1 and
-// i ^ 2; together they reach all 16 lanes.
 __device__ __forceinline__ float slot_max(float a) {
-    a = __builtin_fmaxf(a, row_dpp<0x140>(a));   // row_mirror
-    a = __builtin_fmaxf(a, row_dpp<0x141>(a));   // row_half_mirror
-    a = __builtin_fmaxf(a, row_dpp<0xB1>(a));    // quad_perm [1, 0, 3, 2]
-    a = __builtin_fmaxf(a, row_dpp<0x4E>(a));    // quad_perm [2, 3, 0, 1]
-    return a;
+    uint32_t b = __float_as_uint(a);
+    b = __builtin_elementwise_max(b, row_dpp_u<0x140>(b));   // row_mirror
+    b = __builtin_elementwise_max(b, row_dpp_u<0x141>(b));   // row_half_mirror
+    b = __builtin_elementwise_max(b, row_dpp_u<0xB1>(b));    // quad_perm [1, 0, 3, 2]
+    b = __builtin_elementwise_max(b, row_dpp_u<0x4E>(b));    // quad_perm [2, 3, 0, 1]
+    return __uint_as_float(b);
 }
 
 // Running maximum |v| over a lane's rotated block r.  fmaxf drops a NaN, so a block with a
@@ -127,6 +128,27 @@ __device__ __forceinline__ float block_absmax(const float (&r)[16], float amax) 
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(r[i]));
     return (r[0] - r[0] != 0.0f) ? __builtin_inff() : amax;   // r - r is NaN for inf and NaN
+}
+
+// Maximum of the per-slot maxima smax[s0 .. s0 + ns - 1] (smax 16-byte aligned, at most 16
+// entries).  Every entry is >= +0 or +inf, never NaN (block_absmax maps NaN to +inf), so the
+// bit patterns order as unsigned integers: an integer maximum needs no NaN canonicalisation,
+// and four entries come with one 16-byte read when the range allows it.
+__device__ __forceinline__ float slots_max(const float* smax, int s0, int ns) {
+    const uint32_t* sm = reinterpret_cast<const uint32_t*>(smax);
+    uint32_t m = 0u;
+    if ((s0 & 3) == 0 && (ns & 3) == 0 && s0 + ns <= 16) {
+#pragma unroll
+        for (int s = 0; s < 16; s += 4) {
+            if (s >= ns) break;
+            const uint4 v = *reinterpret_cast<const uint4*>(sm + s0 + s);
+            m = __builtin_elementwise_max(m, __builtin_elementwise_max(__builtin_elementwise_max(v.x, v.y),
+                                                                       __builtin_elementwise_max(v.z, v.w)));
+        }
+    } else {
+        for (int s = s0; s < s0 + ns && s < 16; ++s) m = __builtin_elementwise_max(m, sm[s]);
+    }
+    return __uint_as_float(m);
 }
 
 // A row is poisoned when its maximum is not finite: its scale is NaN and all its codes 0.
