@@ -17,10 +17,9 @@
 //    loads of 8 rows x 128 bytes per stage, no registers or vector instructions.  The
 //    16-byte chunks of a 128-byte row are XOR-swizzled by the row pair, so the MFMA
 //    fragment reads (16 rows, one chunk each) hit 16 distinct bank groups.
-//  - Packed codes come in two stages at a time (a 128-byte line per weight row): lane l
-//    of a load takes 16 bytes = two 16-column groups; the lanes of a row alternate which
-//    stage they hold between consecutive loads, so every lane decodes one piece per stage.
-//    Each piece is decoded with byte permutes against the LDS level-table row of its
+//  - Packed codes come in two stages at a time, one load per stage (16 rows x 64 bytes):
+//    lane l takes 16 bytes = two 16-column groups of a fixed row, so its piece of each stage
+//    sits in a fixed register and needs no selection.  Each piece is decoded with byte permutes against the LDS level-table row of its
 //    group's scale byte and written as two 16-byte fragments into the stage's weight
 //    buffer (same swizzle).
 //  - Pipeline: three activation buffers and three weight buffers.  Stage s multiplies
@@ -160,18 +159,20 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
         for (int j = 0; j < AI; ++j) load_lds16(a_off[j], a_base + s * BK, a_lds + buf * A_STAGE + 1024 * NW * j);
     };
 
-    // ---- code loads: load jj of a wave covers weight rows 8i .. 8i+7 (i = wave + 8jj) of a
-    // 256-deep period, lane (row 8i + lane/8, piece q = (lane%8) ^ 4(jj%2)); piece q holds the
-    // 32 codes of groups 2(q%4), 2(q%4)+1 of the period's stage q/4, and the u16 at 2q of the
-    // row's period scale bytes is their two scale bytes.  Rows past N read row N - 1.
+    // ---- code loads: load t (0/1) of a wave holds stage t of a 256-deep period for weight
+    // rows 16 wave .. 16 wave + 15: lane l takes row 16 wave + l/4 and piece l%4, the 32 codes
+    // of groups 2(l%4), 2(l%4)+1 of the stage (16 of the row's 64 bytes), plus the u16 of
+    // their two scale bytes.  So a lane's piece of stage t is always code register t and its
+    // weight row is fixed.  Rows past N read row N - 1.
+    const int crow = 16 * wave + (lane >> 2), cpair = 2 * (lane & 3);
     const uint8_t* q_base = qp + (int64_t)n0 * KH;
     const uint8_t* s_base = srel + (int64_t)n0 * G;
     uint32_t q_off[CI], s_off[CI];
 #pragma unroll
-    for (int jj = 0; jj < CI; ++jj) {
-        const int n = min(8 * (wave + NW * jj) + (lane >> 3), N - 1 - n0), q = (lane & 7) ^ (4 * (jj & 1));
-        q_off[jj] = (uint32_t)(n * KH + 16 * q);
-        s_off[jj] = (uint32_t)(n * G + 2 * q);
+    for (int t = 0; t < CI; ++t) {
+        const int n = min(crow, N - 1 - n0);
+        q_off[t] = (uint32_t)(n * KH + 64 * t + 8 * cpair);
+        s_off[t] = (uint32_t)(n * G + 8 * t + cpair);
     }
     struct Codes {
         v4u q[CI];
@@ -190,33 +191,28 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
 #pragma unroll
         for (int jj = 0; jj < CI; ++jj) asm volatile("" : "+v"(c.q[jj]), "+v"(c.s[jj]));
     };
-    // the lane's piece of stage t (0/1) of a period: codes, level-table rows, weight row
-    const int hi = (lane >> 2) & 1, cpair = 2 * (lane & 3);
+    // the lane's piece of stage t (0/1, a constant at every use) of a period: codes and
+    // level-table rows
     struct Piece {
         v4u x;
-        int n;
         uint4 t0, t1;
     };
     const uint4* lut4 = reinterpret_cast<const uint4*>(lut);
     auto pick = [&](const Codes& c, int t) __attribute__((always_inline)) {
         Piece p;
-        const bool second = (t ^ hi) != 0;
-        p.x.x = second ? c.q[1].x : c.q[0].x;
-        p.x.y = second ? c.q[1].y : c.q[0].y;
-        p.x.z = second ? c.q[1].z : c.q[0].z;
-        p.x.w = second ? c.q[1].w : c.q[0].w;
-        const uint32_t sc = second ? c.s[1] : c.s[0];
-        p.n = 8 * (wave + (second ? NW : 0)) + (lane >> 3);
+        p.x = t ? c.q[1] : c.q[0];
+        const uint32_t sc = t ? c.s[1] : c.s[0];
         p.t0 = lut4[sc & 0xFF];
         p.t1 = lut4[(sc >> 8) & 0xFF];
         return p;
     };
     // group g (0/1) of a piece: 16 codes -> 16 int8 levels, one fragment of the weight buffer
+    // (row crow, 16-byte chunk cpair + g, swizzled as the activations)
+    const int bw[2] = {128 * crow + 16 * swz(crow, cpair), 128 * crow + 16 * swz(crow, cpair + 1)};
     auto decode_group = [&](const Piece& p, int g, int buf) __attribute__((always_inline)) {
         const uint2 d0 = decode8(g ? p.x.z : p.x.x, g ? p.t1 : p.t0, id);
         const uint2 d1 = decode8(g ? p.x.w : p.x.y, g ? p.t1 : p.t0, id);
-        *reinterpret_cast<v4u*>(Bs + buf * B_STAGE + 128 * p.n + 16 * swz(p.n, cpair + g)) =
-            v4u{d0.x, d0.y, d1.x, d1.y};
+        *reinterpret_cast<v4u*>(Bs + buf * B_STAGE + bw[g]) = v4u{d0.x, d0.y, d1.x, d1.y};
     };
 
     // ---- fragments: lane l holds row (or column) l%16 of a 16-row slice, chunk 4h + l/16 of
@@ -230,12 +226,17 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     struct Frag {
         v4i a[MT], b[NB];
     };
+    // per half: the lane's offsets of its first A and B fragment (the others follow at 2 KiB
+    // steps, within a read instruction's immediate offset)
+    const int a_pos[2] = {16 * ((lane >> 4) ^ rsw) + a_rd[0], 16 * ((4 + (lane >> 4)) ^ rsw) + a_rd[0]};
+    const int b_pos[2] = {16 * ((lane >> 4) ^ rsw) + b_rd[0], 16 * ((4 + (lane >> 4)) ^ rsw) + b_rd[0]};
     auto read_frags = [&](Frag& f, int buf, int h) __attribute__((always_inline)) {
-        const int pos = 16 * ((4 * h + (lane >> 4)) ^ rsw);
+        const int8_t* ab = As + buf * A_STAGE + a_pos[h];
+        const int8_t* bb = Bs + buf * B_STAGE + b_pos[h];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) f.a[mt] = *reinterpret_cast<const v4i*>(As + buf * A_STAGE + pos + a_rd[mt]);
+        for (int mt = 0; mt < MT; ++mt) f.a[mt] = *reinterpret_cast<const v4i*>(ab + 2048 * mt);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) f.b[nb] = *reinterpret_cast<const v4i*>(Bs + buf * B_STAGE + pos + b_rd[nb]);
+        for (int nb = 0; nb < NB; ++nb) f.b[nb] = *reinterpret_cast<const v4i*>(bb + 2048 * nb);
     };
     v4i acc[MT][NB];
 #pragma unroll
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     int buf = 0;   // s % 3
     // steady: 4 <= s <= NS - 5, where every stage around s issues all its loads, so the wait
     // counts are constants
-    auto stage = [&](int s, Codes& nxt, Codes& ld, auto steady_c) __attribute__((always_inline)) {
+    auto stage = [&](int s, Codes& nxt, Codes& ld, auto steady_c, int par) __attribute__((always_inline)) {
         constexpr bool steady = decltype(steady_c)::value;
         const int nbuf = buf == 2 ? 0 : buf + 1, dbuf = nbuf == 2 ? 0 : nbuf + 1;
         const bool dec_on = steady || s + 2 < NS;
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
                 vm_wait_n(after);
             }
             tie(nxt);
-            pc = pick(nxt, (s + 1) & 1);
+            pc = pick(nxt, par);   // (s + 1) & 1
         }
         buf = nbuf;
     };
@@ -375,10 +376,10 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     // period P lives in code slot P % 2 (C0 / C1): stage s picks from period (s + 3) / 2 and
     // even stages load period (s + 4) / 2
     auto quad = [&](int s, auto steady_c) __attribute__((always_inline)) {
-        stage(s + 0, C1, C0, steady_c);
-        stage(s + 1, C0, C0, steady_c);
-        stage(s + 2, C0, C1, steady_c);
-        stage(s + 3, C1, C1, steady_c);
+        stage(s + 0, C1, C0, steady_c, 1);
+        stage(s + 1, C0, C0, steady_c, 0);
+        stage(s + 2, C0, C1, steady_c, 1);
+        stage(s + 3, C1, C1, steady_c, 0);
     };
     int s = 0;
     if (NS >= 4) {
@@ -388,8 +389,8 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     for (; s + 8 <= NS; s += 4) quad(s, Std{});
     for (; s + 4 <= NS; s += 4) quad(s, Dyn{});
     if (s < NS) {
-        stage(s + 0, C1, C0, Dyn{});
-        stage(s + 1, C0, C0, Dyn{});
+        stage(s + 0, C1, C0, Dyn{}, 1);
+        stage(s + 1, C0, C0, Dyn{}, 0);
     }
 
     // ---- epilogue.  Every wave is past the loop's last barrier (no LDS reads remain) and
