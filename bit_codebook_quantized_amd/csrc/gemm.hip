@@ -27,7 +27,8 @@
 //    decoded meanwhile (half per MFMA half, interleaved with the MFMAs), and the codes of
 //    period (s + 4) / 2 are requested on even stages.  One barrier per stage, between the
 //    two MFMA halves: after it the first-half fragments of s + 1 are read while the
-//    second-half MFMAs of s run.
+//    second-half MFMAs of s run.  Steady stages run twelve at a time (the period of the
+//    three buffers and the two code slots), so their LDS offsets are constants.
 //  - Every vector-memory instruction of the main loop is written as inline asm, so the
 //    compiler does not insert waits of its own; each wait below counts the instructions
 //    issued after the one it needs (vmcnt retires in issue order).  Code registers are
@@ -324,13 +325,19 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     int buf = 0;   // s % 3
     // steady: 4 <= s <= NS - 5, where every stage around s issues all its loads, so the wait
     // counts are constants
-    auto stage = [&](int s, Codes& nxt, Codes& ld, auto steady_c, int par) __attribute__((always_inline)) {
+    // par = (s + 1) & 1, a constant at every call; buf_c is the stage's buffer s % 3 when the
+    // caller knows it as a constant (then every LDS offset of the stage is a constant too),
+    // else -1 and the running `buf` is used
+    auto stage = [&](int s, Codes& nxt, Codes& ld, auto steady_c, int par, auto buf_c) __attribute__((always_inline)) {
         constexpr bool steady = decltype(steady_c)::value;
-        const int nbuf = buf == 2 ? 0 : buf + 1, dbuf = nbuf == 2 ? 0 : nbuf + 1;
+        constexpr int BC = decltype(buf_c)::value;
+        const int cb = BC >= 0 ? BC : buf;
+        const bool even = par != 0;   // s is even
+        const int nbuf = cb == 2 ? 0 : cb + 1, dbuf = nbuf == 2 ? 0 : nbuf + 1;
         const bool dec_on = steady || s + 2 < NS;
         // first half: MFMAs of s, second-half fragments of s, first group of B(s + 2)
         mfmas(F0);
-        read_frags(F1, buf, 1);
+        read_frags(F1, cb, 1);
         if (dec_on) decode_group(pc, 0, dbuf);
         interleave();
         __builtin_amdgcn_sched_barrier(0);
@@ -346,8 +353,8 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
             }
             bar_wait_n(after);
         }
-        if (steady || s + 3 < NS) issue_a(s + 3, buf);
-        if (!(s & 1) && (steady || (s + 4) / 2 < NP)) issue_codes(ld, (s + 4) / 2);
+        if (steady || s + 3 < NS) issue_a(s + 3, cb);
+        if (even && (steady || (s + 4) / 2 < NP)) issue_codes(ld, (s + 4) / 2);
         // second half: MFMAs of s, first-half fragments of s + 1, second group of B(s + 2)
         mfmas(F1);
         if (steady || s + 1 < NS) read_frags(F0, nbuf, 0);
@@ -358,7 +365,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
         // prologue before A(1) and A(2) (P = 1)
         if (steady || s + 3 < NS) {
             if (steady) {
-                if (s & 1) vm_wait<AI>();
+                if (!even) vm_wait<AI>();
                 else vm_wait<2 * AI + CV>();
             } else {
                 const int P = (s + 3) / 2;
@@ -373,24 +380,44 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     };
     using Dyn = std::integral_constant<bool, false>;
     using Std = std::integral_constant<bool, true>;
+    using BD = std::integral_constant<int, -1>;
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using B2 = std::integral_constant<int, 2>;
     // period P lives in code slot P % 2 (C0 / C1): stage s picks from period (s + 3) / 2 and
     // even stages load period (s + 4) / 2
     auto quad = [&](int s, auto steady_c) __attribute__((always_inline)) {
-        stage(s + 0, C1, C0, steady_c, 1);
-        stage(s + 1, C0, C0, steady_c, 0);
-        stage(s + 2, C0, C1, steady_c, 1);
-        stage(s + 3, C1, C1, steady_c, 0);
+        stage(s + 0, C1, C0, steady_c, 1, BD{});
+        stage(s + 1, C0, C0, steady_c, 0, BD{});
+        stage(s + 2, C0, C1, steady_c, 1, BD{});
+        stage(s + 3, C1, C1, steady_c, 0, BD{});
+    };
+    // twelve steady stages from s = 4 (mod 12): the buffers (s % 3) and code slots are constants
+    auto dozen = [&](int s) __attribute__((always_inline)) {
+        stage(s + 0, C1, C0, Std{}, 1, B1{});
+        stage(s + 1, C0, C0, Std{}, 0, B2{});
+        stage(s + 2, C0, C1, Std{}, 1, B0{});
+        stage(s + 3, C1, C1, Std{}, 0, B1{});
+        stage(s + 4, C1, C0, Std{}, 1, B2{});
+        stage(s + 5, C0, C0, Std{}, 0, B0{});
+        stage(s + 6, C0, C1, Std{}, 1, B1{});
+        stage(s + 7, C1, C1, Std{}, 0, B2{});
+        stage(s + 8, C1, C0, Std{}, 1, B0{});
+        stage(s + 9, C0, C0, Std{}, 0, B1{});
+        stage(s + 10, C0, C1, Std{}, 1, B2{});
+        stage(s + 11, C1, C1, Std{}, 0, B0{});
     };
     int s = 0;
     if (NS >= 4) {
         quad(0, Dyn{});
         s = 4;
     }
+    for (; s + 16 <= NS; s += 12) dozen(s);
     for (; s + 8 <= NS; s += 4) quad(s, Std{});
     for (; s + 4 <= NS; s += 4) quad(s, Dyn{});
     if (s < NS) {
-        stage(s + 0, C1, C0, Dyn{}, 1);
-        stage(s + 1, C0, C0, Dyn{}, 0);
+        stage(s + 0, C1, C0, Dyn{}, 1, BD{});
+        stage(s + 1, C0, C0, Dyn{}, 0, BD{});
     }
 
     // ---- epilogue.  Every wave is past the loop's last barrier (no LDS reads remain) and
