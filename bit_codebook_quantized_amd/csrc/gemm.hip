@@ -267,14 +267,17 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     // ---- epilogue operands (needed after the loop; the compiler waits for them there)
     constexpr int EV = (BM + 2 * BN + GM_THREADS - 1) / GM_THREADS;
     float ev[EV];
+    // One unconditional load per value from a clamped address, then a select: loads in
+    // separate branches that write the same register would each wait for the previous one.
 #pragma unroll
     for (int e = 0; e < EV; ++e) {
         const int i = tid + GM_THREADS * e;
-        float v = 0.0f;
-        if (i < BM) v = m0 + i < M ? xs[m0 + i] : 0.0f;
-        else if (i < BM + BN) v = n0 + i - BM < N ? ws[n0 + i - BM] : 0.0f;
-        else if (i < BM + 2 * BN) v = (bias && n0 + i - BM - BN < N) ? bias[n0 + i - BM - BN] : 0.0f;
-        ev[e] = v;
+        const bool is_x = i < BM, is_w = !is_x && i < BM + BN, is_b = !is_x && !is_w && i < BM + 2 * BN;
+        const int r = is_x ? m0 + i : n0 + (is_w ? i - BM : i - BM - BN);
+        const bool ok = is_x ? r < M : (is_w || (is_b && bias)) && r < N;
+        const float* src = is_x ? xs : (is_b && bias) ? bias : ws;
+        const float v = src[min(r, (is_x ? M : N) - 1)];
+        ev[e] = ok ? v : 0.0f;
     }
 
     // ---- prologue.  Issue order: codes of period 0, A(0), codes of period 1, A(1), A(2);
@@ -284,6 +287,11 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     auto ops_at = [&](int t) __attribute__((always_inline)) {
         return (t + 3 < NS ? AI : 0) + ((!(t & 1) && (t + 4) / 2 < NP) ? CV : 0);
     };
+    // The codebook (uniform loads) is requested before the tile's loads: behind ~100 KB of
+    // loads per CU it would arrive ~2 us later and hold up the level table.
+    float cb[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) cb[c] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(codebook[c])));
     Codes C0, C1;
     issue_codes(C0, 0);
     issue_a(0, 0);
@@ -293,12 +301,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     const int after_a1 = NS > 2 ? AI : 0;
     const int after_p1 = (NS > 1 ? AI : 0) + after_a1;
     const int after_a0 = (NP > 1 ? CV : 0) + after_p1;
-    {
-        float cb[16];   // uniform loads
-#pragma unroll
-        for (int c = 0; c < 16; ++c) cb[c] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(codebook[c])));
-        build_level_table_regs(lut, cb, tid, GM_THREADS);
-    }
+    build_level_table_regs(lut, cb, tid, GM_THREADS);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // level table
     vm_wait_n(AI + after_a0);
     tie(C0);
