@@ -280,8 +280,9 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
         ev[e] = ok ? v : 0.0f;
     }
 
-    // ---- prologue.  Issue order: codes of period 0, A(0), codes of period 1, A(1), A(2);
-    // then stage t issues A(t + 3) and, when t is even, the codes of period (t + 4) / 2.
+    // ---- prologue.  Issue order: codes of period 0, A(0), codes of period 1, A(1), A(2)
+    // (the last three after the level table is built and B(0), B(1) are decoded); then
+    // stage t issues A(t + 3) and, when t is even, the codes of period (t + 4) / 2.
     // ops_at(t) counts stage t's vector-memory instructions; every wait counts the
     // instructions issued after the one it needs.
     auto ops_at = [&](int t) __attribute__((always_inline)) {
@@ -292,18 +293,14 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     float cb[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) cb[c] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(codebook[c])));
+    // Only the first period's codes and A(0) go out before the level table is built and
+    // B(0), B(1) are decoded; the rest of the prologue's loads follow (same issue order).
     Codes C0, C1;
     issue_codes(C0, 0);
     issue_a(0, 0);
-    if (NP > 1) issue_codes(C1, 1);
-    if (NS > 1) issue_a(1, 1);
-    if (NS > 2) issue_a(2, 2);
-    const int after_a1 = NS > 2 ? AI : 0;
-    const int after_p1 = (NS > 1 ? AI : 0) + after_a1;
-    const int after_a0 = (NP > 1 ? CV : 0) + after_p1;
     build_level_table_regs(lut, cb, tid, GM_THREADS);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // level table
-    vm_wait_n(AI + after_a0);
+    vm_wait<AI>();   // C0 landed (A(0) may still be in flight)
     tie(C0);
     {
         const Piece p0 = pick(C0, 0);
@@ -315,6 +312,12 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
             decode_group(p1, 1, 1);
         }
     }
+    if (NP > 1) issue_codes(C1, 1);
+    if (NS > 1) issue_a(1, 1);
+    if (NS > 2) issue_a(2, 2);
+    const int after_a1 = NS > 2 ? AI : 0;
+    const int after_p1 = (NS > 1 ? AI : 0) + after_a1;
+    const int after_a0 = (NP > 1 ? CV : 0) + after_p1;
     Piece pc;   // the piece of B(s + 2) during stage s
     if (NS > 2) {
         vm_wait_n(after_p1);
