@@ -281,7 +281,8 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     }
 
     // ---- prologue.  Issue order: codes of period 0, A(0), codes of period 1, A(1), A(2)
-    // (the last three after the level table is built and B(0), B(1) are decoded); then
+    // (the first two after the level table is built, the last three after B(0), B(1) are
+    // decoded); then
     // stage t issues A(t + 3) and, when t is even, the codes of period (t + 4) / 2.
     // ops_at(t) counts stage t's vector-memory instructions; every wait counts the
     // instructions issued after the one it needs.
@@ -293,12 +294,13 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_kernel(
     float cb[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) cb[c] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(codebook[c])));
-    // Only the first period's codes and A(0) go out before the level table is built and
-    // B(0), B(1) are decoded; the rest of the prologue's loads follow (same issue order).
+    // The level table is built first (it waits only for the codebook), then the first
+    // period's codes and A(0) go out, and the rest of the prologue's loads follow the decode
+    // of B(0), B(1) (the same issue order throughout).
     Codes C0, C1;
+    build_level_table_regs(lut, cb, tid, GM_THREADS);
     issue_codes(C0, 0);
     issue_a(0, 0);
-    build_level_table_regs(lut, cb, tid, GM_THREADS);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // level table
     vm_wait<AI>();   // C0 landed (A(0) may still be in flight)
     tie(C0);

@@ -249,10 +249,14 @@ def test_layer_outputs_of_non_finite_rows_are_nan():
 # (1300, 512, 256): 6 x 4 tiles, so the tile order has a band of 4 row tiles and a short
 # band of 2 (and 24 tiles take the XCD grouping).  K sets the number of 128-deep stages of
 # the software pipeline: 2, 4, 6 (a 4-stage group and a 2-stage tail), 10, 12 and 18 (a
-# first group, steady groups with constant wait counts, a last group and a tail), 24, 32.
+# first group, steady groups with constant wait counts, a last group and a tail), 24 (one
+# 12-stage steady body with constant buffers, then a steady 4-stage group), 32 (two 12-stage
+# bodies), 36 (two bodies, a steady group, a last group) and 42 (two bodies, two steady
+# groups, a last group and a tail).
 GEMM_SHAPES = [(16, 256, 256), (37, 200, 768), (300, 1000, 512), (257, 129, 256), (1, 128, 4096),
                (9, 64, 256), (513, 384, 1024), (64, 4096, 3072), (256, 256, 256), (512, 260, 512),
-               (1300, 512, 256), (300, 384, 1280), (513, 260, 1536), (200, 256, 2304)]
+               (1300, 512, 256), (300, 384, 1280), (513, 260, 1536), (200, 256, 2304),
+               (257, 129, 4608), (130, 300, 5376)]
 
 
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
