@@ -305,6 +305,11 @@ def bench_gemv(args, torch, B, device):
         two_ms, _ = timed_launches(torch, two, args.gemv_launches, sleep)
         act = [B.prepared_gemv_act(x, layers[c], out) for c in range(copies)]
         act_ms, _ = timed_launches(torch, act, args.gemv_launches, sleep)
+        # the 64 copies as independent layers of one w4a8_gemv_grouped launch (605 MB of
+        # weights per launch: the kernel's streaming rate at this M without per-launch cost)
+        gouts = [torch.empty(m, N, dtype=torch.bfloat16, device=device) for _ in range(copies)]
+        grouped = [B.prepared_gemv_grouped([(xq, xs, layers[c], gouts[c]) for c in range(copies)])]
+        grp_ms = median_trials(torch, grouped, 10, 5, sleep // 4)
         wb = weight_bytes(N, K)
         res[str(m)] = dict(
             gemv_us=round(cold_ms * 1e3, 3),
@@ -318,6 +323,9 @@ def bench_gemv(args, torch, B, device):
             layer_gemv_act_us=round(act_ms * 1e3, 3),
             layer_gemv_act_weight_GBps=round(wb / (act_ms * 1e-3) / 1e9, 1),
             host_enqueue_us=round(enq / per_trial * 1e6, 2),
+            grouped_64_copies_us=round(grp_ms * 1e3, 1),
+            grouped_64_copies_weight_GBps=round(copies * wb / (grp_ms * 1e-3) / 1e9, 1),
+            grouped_64_copies_frac=round(copies * wb / (grp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         )
     return res
 
