@@ -137,6 +137,7 @@ hipError_t launch_rotate_quant(const uint16_t* x, int64_t M, int K, int qmax, in
     const dim3 g((unsigned)grid), b((unsigned)threads);
     if (nch <= 1) hipLaunchKernelGGL(rotate_quant_kernel<1>, g, b, 0, stream, x, M, K, qmax, xq, xs);
     else if (nch <= 2) hipLaunchKernelGGL(rotate_quant_kernel<2>, g, b, 0, stream, x, M, K, qmax, xq, xs);
+    else if (nch <= 3) hipLaunchKernelGGL(rotate_quant_kernel<3>, g, b, 0, stream, x, M, K, qmax, xq, xs);
     else if (nch <= 4) hipLaunchKernelGGL(rotate_quant_kernel<4>, g, b, 0, stream, x, M, K, qmax, xq, xs);
     else if (nch <= 8) hipLaunchKernelGGL(rotate_quant_kernel<8>, g, b, 0, stream, x, M, K, qmax, xq, xs);
     else hipLaunchKernelGGL(rotate_quant_kernel<0>, g, b, 0, stream, x, M, K, qmax, xq, xs);
