@@ -162,8 +162,22 @@ def bench_prefill(args, torch, B, device):
     rq_ms, _ = timed_launches(torch, [rq_call], 20, int(args.sleep_cycles))
     # the GEMM alone: median of 5 trials of 100 back-to-back launches (one event pair each)
     gemm_med_ms = median_trials(torch, [gemm_call], 100, 5, int(args.sleep_cycles))
+    # The same launches on operands that toggle fewer bits: a copy of the layer whose scale
+    # bytes are 0 (every decoded weight 0) and all-zero activations.  The instruction stream is
+    # identical; at full load the chip's clock follows the operands' switching power, so the
+    # difference is what the power budget costs this kernel (outputs of these runs are unused).
+    zero_layer = B.W4A8Layer(layer.qpacked, torch.zeros_like(layer.srel), layer.codebook, layer.s_channel)
+    xq_zero = torch.zeros_like(xq)
+    zw_call = B.prepared_linear("w4a8_gemm", xq, xs, zero_layer, out)
+    za_call = B.prepared_linear("w4a8_gemm", xq_zero, xs, layer, out)
+    operands = {"random_us": round(gemm_med_ms * 1e3, 2),
+                "zero_weights_us": round(median_trials(torch, [zw_call], 100, 5, int(args.sleep_cycles)) * 1e3, 2),
+                "zero_activations_us": round(median_trials(torch, [za_call], 100, 5, int(args.sleep_cycles)) * 1e3, 2),
+                "note": "w4a8_gemm back to back, median of 5 x 100, same launches on all-zero operands"}
+    del zw_call, za_call, zero_layer, xq_zero
     ops = 2.0 * M * N * K
     return dict(M=M, N=N, K=K, wall_s=wall, graph_wall_s=graph_wall, rq_ms=rq_ms, gemm_ms=gemm_ms, gemm_med_ms=gemm_med_ms, ops=ops,
+                operands=operands,
                 x_np=x_np, host=host, quant_ms=quant_ms,
                 rq_bytes=3 * M * K + 4 * M,
                 gemm_bytes=weight_bytes(N, K) + M * K + 4 * M + 2 * M * N)
@@ -591,6 +605,7 @@ def main():
                      "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": measured_traffic(),
                      "kernel": "w4a8_gemm", "kernel_us": round(pre["gemm_ms"] * 1e3, 3),
                      "kernel_us_median_5x100": round(pre["gemm_med_ms"] * 1e3, 3)},
+        "gemm_operand_dependence": pre["operands"],
         "quantize_w4": {"us": round(pre["quant_ms"] * 1e3, 1), "layer": "4096 x 4096 fp32, rotated on the fly",
                         "Mweights_per_s": round(pre["N"] * pre["K"] / (pre["quant_ms"] * 1e-3) / 1e6, 1),
                         "note": "offline weight quantisation, not part of the step"},
