@@ -18,7 +18,7 @@ Sources.  Each function cites the page and the function or section it follows:
 Precision.  The pages fix fp32 for the stored scales, the decode product, the
 quantizer's divisions and the epilogue; the oracle does those steps in numpy
 float32 (IEEE, round-to-nearest-even, no fused multiply-add).  Where the pages
-leave the precision open the oracle uses the readings listed in the design doc:
+leave the precision open the oracle takes these readings:
 
   * rotation: the exact block product rounded once to fp32 (fp64 where that
     is provably exact, Python integers otherwise; a block with an infinite or
