@@ -553,7 +553,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the path shards along N; "
-              "multi-GPU runs are outside this build)", file=sys.stderr)
+              "this benchmark measures one GPU)", file=sys.stderr)
         sys.exit(2)
     import torch
     from bit_codebook_quantized_amd import w4a8 as B
